@@ -1,0 +1,108 @@
+"""Seeded synthetic inputs for the GDN decode step, shared by the tests and the benchmark.
+
+This module only draws random numbers and shapes them into the input recipe of each workload:
+it holds none of the step's arithmetic and computes no expected value. The GPU library and the
+oracle both consume what it returns; neither is imported here.
+
+Recipes (no trained weights or live activations exist for this path, so these stand in):
+  * Decode-step workloads take q, k already L2-normalised and the gates as values:
+      state  ~ N(0, std)            (std 0.02; "zeros" for the tiny workload)
+      q, k   ~ N(0, 1), each (sequence, token, head) vector scaled to unit length in fp64
+      v      ~ N(0, 1)
+      beta   = logistic(z),                z ~ N(0, 1)
+      alpha  = exp(-softplus(z + shift)),  z ~ N(0, 1)   (shift 2 by default)
+    draw order: state, q, k, v, beta-logit, alpha-logit; one PCG64 stream per workload.
+  * Fused-layer workloads take raw activations:
+      qkv ~ N(0, 1) bf16 [B,T,C], conv_state ~ N(0, 1) bf16 [B,C,3], conv_w ~ N(0, 0.5) fp32 [C,4],
+      a_logit, b_logit ~ N(0, 1) fp32 [B,T,H], state ~ N(0, 0.02)
+    draw order: qkv, conv_state, conv_w, a_logit, b_logit, state.
+Every narrower type is the round-to-nearest-even image of the fp32/fp64 draw (torch's cast).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+# Named workloads: batch B, heads H, head dim D (dk = dv), tokens per call T.
+WORKLOADS = {
+    "decode_b1_h2_d16_t8": dict(B=1, H=2, D=16, T=8, act="f32", state_init="zeros"),
+    "decode_b1_h48_d128_t1": dict(B=1, H=48, D=128, T=1, act="bf16", state_init="normal"),
+    "decode_b64_h48_d128_t1": dict(B=64, H=48, D=128, T=1, act="bf16", state_init="normal"),
+    "decode_b256_h48_d128_t1": dict(B=256, H=48, D=128, T=1, act="bf16", state_init="normal"),
+    "fused_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, fused=True),
+}
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _unit_rows(a: np.ndarray) -> np.ndarray:
+    """Scale every last-axis vector of a float64 array to unit Euclidean length."""
+    return a / np.sqrt(np.sum(a * a, axis=-1, keepdims=True))
+
+
+def _cast(a: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(_TORCH_DTYPES[dtype])
+
+
+def decode_inputs(B: int, H: int, D: int, T: int, *, act: str = "bf16",
+                  state_dtype: str = "f32", state_init: str = "normal",
+                  state_std: float = 0.02, alpha_shift: float = 2.0, seed: int = 0) -> dict:
+    """Inputs of one decode-step call, as CPU torch tensors in their device dtypes."""
+    rng = _rng(seed)
+    if state_init == "normal":
+        s = rng.standard_normal((B, H, D, D), dtype=np.float32)
+        s *= np.float32(state_std)
+    elif state_init == "zeros":
+        s = np.zeros((B, H, D, D), dtype=np.float32)
+    else:
+        raise ValueError(f"unknown state_init {state_init!r}")
+    q = _unit_rows(rng.standard_normal((B, T, H, D)))
+    k = _unit_rows(rng.standard_normal((B, T, H, D)))
+    v = rng.standard_normal((B, T, H, D))
+    zb = rng.standard_normal((B, T, H))
+    za = rng.standard_normal((B, T, H)) + alpha_shift
+    beta = 1.0 / (1.0 + np.exp(-zb))
+    alpha = np.exp(-(np.maximum(za, 0.0) + np.log1p(np.exp(-np.abs(za)))))
+    return dict(
+        q=_cast(q.astype(np.float32), act), k=_cast(k.astype(np.float32), act),
+        v=_cast(v.astype(np.float32), act),
+        alpha=_cast(alpha.astype(np.float32), "f32"), beta=_cast(beta.astype(np.float32), "f32"),
+        state=_cast(s, state_dtype),
+        B=B, H=H, D=D, T=T, act=act, state_dtype=state_dtype,
+    )
+
+
+def fused_inputs(B: int, H: int, D: int, T: int, *, state_dtype: str = "f32",
+                 state_std: float = 0.02, conv_w_std: float = 0.5, with_bias: bool = False,
+                 seed: int = 0) -> dict:
+    """Inputs of one fused-layer call (conv + gates + T steps), CPU torch tensors."""
+    rng = _rng(seed)
+    C = 3 * H * D
+    qkv = rng.standard_normal((B, T, C), dtype=np.float32)
+    cs = rng.standard_normal((B, C, 3), dtype=np.float32)
+    w = rng.standard_normal((C, 4), dtype=np.float32) * np.float32(conv_w_std)
+    a = rng.standard_normal((B, T, H), dtype=np.float32)
+    b = rng.standard_normal((B, T, H), dtype=np.float32)
+    s = rng.standard_normal((B, H, D, D), dtype=np.float32)
+    s *= np.float32(state_std)
+    bias = rng.standard_normal((C,), dtype=np.float32) * np.float32(0.1) if with_bias else None
+    return dict(
+        qkv=_cast(qkv, "bf16"), conv_state=_cast(cs, "bf16"), conv_w=_cast(w, "f32"),
+        conv_b=None if bias is None else _cast(bias, "f32"),
+        a_logit=_cast(a, "f32"), b_logit=_cast(b, "f32"), state=_cast(s, state_dtype),
+        B=B, H=H, D=D, T=T, state_dtype=state_dtype,
+    )
+
+
+def workload_inputs(name: str, *, seed: int = 0, **overrides) -> dict:
+    """Inputs of a named workload (see WORKLOADS); keyword overrides replace recipe fields."""
+    spec = dict(WORKLOADS[name])
+    fused = spec.pop("fused", False)
+    spec.update(overrides)
+    if fused:
+        return fused_inputs(seed=seed, **spec)
+    return decode_inputs(seed=seed, **spec)
