@@ -1,0 +1,278 @@
+"""Benchmark of the GDN recurrent decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one layer's call of the hot path over one batch of seeded synthetic input that is
+already resident in HBM: gdn_decode_step for the decode workloads (state read once, T tokens,
+state written once), gdn_conv_gate_decode for the fused one. Layer buffers (state, inputs,
+outputs) are rotated so that the state a step reads was not left in the 256 MB MALL by the
+previous step. W untimed steps, then K timed steps between two device synchronisations; the
+HIP events that time them are recorded on the stream the kernels are launched on.
+
+Prints ONE JSON line. `value` is microseconds per layer step (lower is better); `roofline`
+prices the kernel's algorithmic bytes per launch against MI355X's 8 TB/s HBM peak; `traffic`
+is the measured HBM bytes per launch from a committed rocprofv3 counter summary, or null if
+the kernel source changed since it was taken; `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same workload on the host.
+
+`--workload copy_<MB>` instead times a plain device-to-device copy of that many MB (torch's
+copy kernel), the calibration used for the counter-based traffic and the practical
+read+write bandwidth ceiling.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN decode µs/layer + achieved HBM GB/s (% roofline), B=256 H=48 128×128"
+DEFAULT_WORKLOAD = "decode_b256_h48_d128_t1"
+PEAK_HBM_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_deltanet_recurrent_02_amd", "csrc", f)
+                  for f in ("gdn_kernels.hip", "gdn_launch.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--layers", type=int, default=0, help="layer buffers rotated (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
+    return ap.parse_args(argv)
+
+
+# ----------------------------------------------------------------------------- bytes
+
+
+def algorithmic_bytes(spec: dict, state_dtype: str) -> int:
+    """Bytes the step must move once: state read + written, per-token vectors, outputs."""
+    B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
+    sb = 4 if state_dtype == "f32" else 2
+    state = 2 * B * H * D * D * sb
+    if spec.get("fused"):
+        C = 3 * H * D
+        return (state + B * T * C * 2          # qkv in
+                + 2 * B * C * 3 * 2            # conv state read + write
+                + C * 4 * 4                    # conv weights
+                + 2 * B * T * H * 4            # gate logits
+                + B * T * H * D * 2)           # o
+    ab = 4 if spec["act"] == "f32" else 2
+    return state + B * T * H * (3 * D * ab + 8 + D * ab)
+
+
+def flops(spec: dict) -> int:
+    """Arithmetic of the recurrence: u = S k, S q (2 x 2D^2), update (2D^2), k.q, delta, o."""
+    B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
+    return B * H * T * (6 * D * D + 6 * D)
+
+
+def read_traffic(workload: str, state_dtype: str):
+    """Measured HBM bytes per launch from profiles/traffic_<workload>_<state>.txt, if the
+    kernel source still hashes to the value recorded there; else None."""
+    path = os.path.join(PROFILES, f"traffic_{workload}_{state_dtype}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- GPU timing
+
+
+def time_gpu(args, spec, workload):
+    import torch
+
+    import gated_deltanet_recurrent_02_amd as gdn
+    from gated_deltanet_recurrent_02_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fused = spec.get("fused", False)
+    x = synth.workload_inputs(workload, state_dtype=args.state_dtype)
+    state_bytes = x["state"].numel() * x["state"].element_size()
+    L = args.layers or max(1, math.ceil(2 * MALL_BYTES / state_bytes))
+    L = min(L, 64)
+    print(f"[bench] {workload} state={args.state_dtype} layers={L} "
+          f"state_bytes={state_bytes}", file=sys.stderr, flush=True)
+    layers = []
+    for i in range(L):
+        g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+        if i > 0:  # every layer has its own state; copies of the same draw are enough
+            g["state"] = g["state"].clone()
+        if fused:
+            g["o"] = torch.empty((x["B"], x["T"], x["H"], x["D"]), dtype=torch.bfloat16, device=dev)
+        else:
+            g["o"] = torch.empty_like(g["v"])
+        layers.append(g)
+    del x
+
+    if fused:
+        def step(g):
+            gdn.conv_gate_decode(g["qkv"], g["conv_state"], g["conv_w"], g["conv_b"], g["a_logit"],
+                                 g["b_logit"], g["state"], o=g["o"])
+    else:
+        def step(g):
+            gdn.decode_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state"], o=g["o"])
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(layers[i % L])
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(layers[i % L])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    return ms_total / args.steps, L
+
+
+def time_copy(args, mb: int):
+    import torch
+    dev = torch.device("cuda:0")
+    n = (mb << 20) // 4
+    L = max(2, math.ceil(2 * MALL_BYTES / (n * 4)))
+    src = [torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(L)]
+    dst = [torch.empty_like(s) for s in src]
+    for i in range(args.warmup):
+        dst[i % L].copy_(src[i % L])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        dst[i % L].copy_(src[i % L])
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / args.steps, 2 * n * 4
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline(spec: dict, workload: str, state_dtype: str, target_s: float):
+    """The fp64 oracle, untuned, on a bounded sample: the first few sequences of the same
+    workload (all heads), repeated until about `target_s` seconds; scaled to one layer."""
+    import numpy as np
+
+    import oracle
+    from gated_deltanet_recurrent_02_amd import synth
+
+    B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
+    Bs = max(1, min(B, 8))
+    x = synth.workload_inputs(workload, state_dtype=state_dtype, B=Bs)
+    f = lambda t: t.double().numpy()
+    if spec.get("fused"):
+        args = (f(x["qkv"]), f(x["conv_state"]), f(x["conv_w"]), None, f(x["a_logit"]),
+                f(x["b_logit"]), f(x["state"]))
+        run = lambda: oracle.gdn_conv_gate_decode(*args, H=H, dk=D, dv=D)
+    else:
+        args = tuple(f(x[n]) for n in ("q", "k", "v", "alpha", "beta", "state"))
+        run = lambda: oracle.gdn_decode(*args)
+    oracle.load()
+    run()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    per_rep = el / reps
+    us_per_layer = per_rep * (B / Bs) * 1e6
+    return {"value": us_per_layer, "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{Bs} of {B} sequences x {H} heads (D={D}, T={T}), fp64 single-thread C "
+                      f"oracle, {reps} repetitions in {el:.1f} s, scaled by {B}/{Bs}",
+            "host_cpus": os.cpu_count()}
+
+
+# ----------------------------------------------------------------------------- main
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path has no cross-GPU step; see the sharding note in the design document)",
+              file=sys.stderr)
+        return 2
+
+    if args.workload.startswith("copy_"):
+        mb = int(args.workload.split("_", 1)[1])
+        ms, nbytes = time_copy(args, mb)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        print(json.dumps({"metric": "device copy GB/s (read + write)", "value": gbps, "unit": "GB/s",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+                          "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                          "config": {"workload": args.workload, "bytes_per_copy": nbytes}}))
+        return 0
+
+    from gated_deltanet_recurrent_02_amd import synth
+    spec = dict(synth.WORKLOADS[args.workload])
+    ms, L = time_gpu(args, spec, args.workload)
+    us = ms * 1e3
+    nbytes = algorithmic_bytes(spec, args.state_dtype)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
+    act = "bf16" if spec.get("fused") else spec["act"]
+    line = {
+        "metric": METRIC, "value": us, "unit": "us/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "dk": D, "dv": D, "T": T,
+                   "state_dtype": args.state_dtype, "act_dtype": act,
+                   "entry_point": "gdn_conv_gate_decode" if spec.get("fused") else "gdn_decode_step",
+                   "layers_rotated": L},
+        "achieved_gbps": gbps,
+        "seq_tokens_per_s": B * T / (ms * 1e-3),
+        "us_per_token_48_layers": us * 48,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": gbps / PEAK_HBM_GBPS, "traffic": read_traffic(args.workload, args.state_dtype),
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "kernel_source_sha256_16": kernel_source_hash()},
+        "gflops": flops(spec) / (ms * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(spec, args.workload, args.state_dtype, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,42 @@
+"""Build libgdn.so in-tree with hipcc for gfx950.
+
+    python -m gated_deltanet_recurrent_02_amd.build        # or __graft_entry__.build()
+
+The library is the hand-written HIP kernels plus the C-ABI layer; it links only the HIP
+runtime. Packed-fp32 instruction selection is switched off (-packed-fp32-ops).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(PKG, "libgdn.so")
+SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_api.cpp")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HIPFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def build(output: str = LIBRARY, extra_flags: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile the kernels and the C ABI into one shared library; returns its path."""
+    tmp = output + ".tmp"
+    cmd = [HIPCC, *HIPFLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

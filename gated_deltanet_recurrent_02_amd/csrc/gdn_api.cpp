@@ -1,0 +1,230 @@
+// C-ABI entry points of libgdn.so (declared in include/gdn.h): host-side validation, then a
+// kernel launch on the caller's stream. Nothing here synchronises or allocates except
+// gdn_state_alloc / gdn_state_free.
+
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+gdn_status fail_hip(const char* what, hipError_t e) {
+    g_last_error = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+    return GDN_ERR_HIP;
+}
+
+bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_dtype(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
+size_t dtype_bytes(gdn_dtype t) { return t == GDN_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b with overflow detection on size_t.
+bool mul_ok(size_t a, size_t b, size_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char* name, const void* p, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, lo + bytes};
+}
+
+bool overlaps(const Range& a, const Range& b) {
+    return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+// Shape checks shared by the two step functions. Returns GDN_OK, or a failure with message.
+gdn_status check_shape(const char* fn, int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv) {
+    if (B < 0 || T < 0) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": B and T must be >= 0");
+    if (H < 1) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": H must be >= 1");
+    if (dk < 1 || dv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": dk and dv must be >= 1");
+    if (dk != dv || !supported_dim(dk))
+        return fail(GDN_ERR_UNSUPPORTED,
+                    std::string(fn) + ": supported head dims are dk == dv in {16, 32, 64, 128}, got dk=" +
+                        std::to_string(dk) + " dv=" + std::to_string(dv));
+    if (B * (int64_t)H >= (int64_t(1) << 31))
+        return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": B * H must be < 2^31");
+    return GDN_OK;
+}
+
+gdn_status check_ptrs(const char* fn, std::initializer_list<std::pair<const char*, const void*>> ps) {
+    for (auto& p : ps) {
+        if (p.second == nullptr)
+            return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": " + p.first + " is NULL");
+        if (!aligned16(p.second))
+            return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": " + p.first + " is not 16-byte aligned");
+    }
+    return GDN_OK;
+}
+
+gdn_status check_disjoint(const char* fn, const Range& out, std::initializer_list<Range> others) {
+    for (auto& r : others)
+        if (overlaps(out, r))
+            return fail(GDN_ERR_INVALID_ARGUMENT,
+                        std::string(fn) + ": " + out.name + " overlaps " + r.name);
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_INVALID_ARGUMENT: return "GDN_ERR_INVALID_ARGUMENT";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+        case GDN_ERR_OUT_OF_MEMORY: return "GDN_ERR_OUT_OF_MEMORY";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    }
+    return "unknown";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+gdn_status gdn_state_alloc(int64_t B, int32_t H, int32_t dk, int32_t dv, gdn_dtype state_dtype,
+                           void** state_out, size_t* bytes_out) {
+    g_last_error.clear();
+    if (!state_out) return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_state_alloc: state_out is NULL");
+    *state_out = nullptr;
+    if (B < 1 || H < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_state_alloc: B and H must be >= 1");
+    if (!valid_dtype(state_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_state_alloc: bad state_dtype");
+    if (dk != dv || !supported_dim(dk))
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_state_alloc: supported head dims are dk == dv in {16, 32, 64, 128}");
+    size_t bytes = 0;
+    if (!mul_ok((size_t)B, (size_t)H, &bytes) || !mul_ok(bytes, (size_t)dk * dv, &bytes) ||
+        !mul_ok(bytes, dtype_bytes(state_dtype), &bytes))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_state_alloc: size overflows");
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) {
+        (void)hipGetLastError();
+        return fail(GDN_ERR_OUT_OF_MEMORY, "gdn_state_alloc: hipMalloc of " + std::to_string(bytes) +
+                                               " bytes failed: " + hipGetErrorString(e));
+    }
+    if (e != hipSuccess) return fail_hip("gdn_state_alloc: hipMalloc", e);
+    e = hipMemset(p, 0, bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return fail_hip("gdn_state_alloc: zero fill", e);
+    }
+    *state_out = p;
+    if (bytes_out) *bytes_out = bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_state_free(void* state) {
+    g_last_error.clear();
+    if (!state) return GDN_OK;
+    hipError_t e = hipFree(state);
+    if (e != hipSuccess) return fail_hip("gdn_state_free: hipFree", e);
+    return GDN_OK;
+}
+
+gdn_status gdn_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                           const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                           const float* alpha, const float* beta,
+                           void* state, gdn_dtype state_dtype,
+                           void* o, float scale, void* stream) {
+    static const char* fn = "gdn_decode_step";
+    g_last_error.clear();
+    gdn_status s = check_shape(fn, B, T, H, dk, dv);
+    if (s != GDN_OK) return s;
+    if (!valid_dtype(act_dtype) || !valid_dtype(state_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": bad dtype");
+    if (B == 0 || T == 0) return GDN_OK;
+    s = check_ptrs(fn, {{"q", q}, {"k", k}, {"v", v}, {"alpha", alpha}, {"beta", beta},
+                        {"state", state}, {"o", o}});
+    if (s != GDN_OK) return s;
+    const size_t tokens = (size_t)B * T * H;
+    const size_t ab = dtype_bytes(act_dtype);
+    const size_t state_bytes = (size_t)B * H * dk * dv * dtype_bytes(state_dtype);
+    Range ro = range("o", o, tokens * dv * ab);
+    s = check_disjoint(fn, ro, {range("q", q, tokens * dk * ab), range("k", k, tokens * dk * ab),
+                                range("v", v, tokens * dv * ab), range("alpha", alpha, tokens * 4),
+                                range("beta", beta, tokens * 4), range("state", state, state_bytes)});
+    if (s != GDN_OK) return s;
+    Range rs = range("state", state, state_bytes);
+    s = check_disjoint(fn, rs, {range("q", q, tokens * dk * ab), range("k", k, tokens * dk * ab),
+                                range("v", v, tokens * dv * ab), range("alpha", alpha, tokens * 4),
+                                range("beta", beta, tokens * 4)});
+    if (s != GDN_OK) return s;
+
+    gdn::DecodeArgs a;
+    a.B = B; a.T = T; a.H = H; a.D = dk;
+    a.q = q; a.k = k; a.v = v;
+    a.act = act_dtype == GDN_F32 ? gdn::DType::F32 : gdn::DType::BF16;
+    a.alpha = alpha; a.beta = beta;
+    a.state = state;
+    a.state_dtype = state_dtype == GDN_F32 ? gdn::DType::F32 : gdn::DType::BF16;
+    a.o = o; a.scale = scale;
+    hipError_t e = gdn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip("gdn_decode_step: kernel launch", e);
+    return GDN_OK;
+}
+
+gdn_status gdn_conv_gate_decode(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                const void* qkv, void* conv_state,
+                                const float* conv_w, const float* conv_b,
+                                const float* a_logit, const float* b_logit,
+                                void* state, gdn_dtype state_dtype,
+                                void* o, float scale, float l2_eps, void* stream) {
+    static const char* fn = "gdn_conv_gate_decode";
+    g_last_error.clear();
+    gdn_status s = check_shape(fn, B, T, H, dk, dv);
+    if (s != GDN_OK) return s;
+    if (!valid_dtype(state_dtype)) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": bad dtype");
+    if (!(l2_eps >= 0.0f)) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": l2_eps must be >= 0");
+    if (B == 0 || T == 0) return GDN_OK;
+    s = check_ptrs(fn, {{"qkv", qkv}, {"conv_state", conv_state}, {"conv_w", conv_w},
+                        {"a_logit", a_logit}, {"b_logit", b_logit}, {"state", state}, {"o", o}});
+    if (s != GDN_OK) return s;
+    if (conv_b && !aligned16(conv_b))
+        return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": conv_b is not 16-byte aligned");
+    const size_t C = (size_t)H * (dk + dk + dv);
+    const size_t tokens = (size_t)B * T * H;
+    const size_t state_bytes = (size_t)B * H * dk * dv * dtype_bytes(state_dtype);
+    const Range r_qkv = range("qkv", qkv, (size_t)B * T * C * 2);
+    const Range r_cs = range("conv_state", conv_state, (size_t)B * C * 3 * 2);
+    const Range r_w = range("conv_w", conv_w, C * 16);
+    const Range r_b = range("conv_b", conv_b, conv_b ? C * 4 : 0);
+    const Range r_a = range("a_logit", a_logit, tokens * 4);
+    const Range r_bl = range("b_logit", b_logit, tokens * 4);
+    const Range r_s = range("state", state, state_bytes);
+    const Range r_o = range("o", o, tokens * dv * 2);
+    s = check_disjoint(fn, r_o, {r_qkv, r_cs, r_w, r_b, r_a, r_bl, r_s});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_cs, {r_qkv, r_w, r_b, r_a, r_bl, r_s});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_s, {r_qkv, r_w, r_b, r_a, r_bl});
+    if (s != GDN_OK) return s;
+
+    gdn::FusedArgs a;
+    a.B = B; a.T = T; a.H = H; a.D = dk;
+    a.qkv = qkv; a.conv_state = conv_state; a.conv_w = conv_w; a.conv_b = conv_b;
+    a.a_logit = a_logit; a.b_logit = b_logit;
+    a.state = state;
+    a.state_dtype = state_dtype == GDN_F32 ? gdn::DType::F32 : gdn::DType::BF16;
+    a.o = o; a.scale = scale; a.l2_eps = l2_eps;
+    hipError_t e = gdn::launch_conv_gate_decode(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip("gdn_conv_gate_decode: kernel launch", e);
+    return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,490 @@
+// HIP kernels for the Gated DeltaNet (GDN) recurrent decode step on gfx950 (CDNA4).
+//
+// The step, per (sequence b, head h) and token t ("GDN tuning limits on Kunlun XPU", section
+// 二 背景: a rank-1 update of the per-head state with a decay, after conv and gating):
+//     u = S k,   delta = beta (v - alpha u),   S <- alpha S + delta k^T,
+//     o = S_new (scale q) = alpha (S q) + delta (k . q)
+// which is S_t = alpha S_{t-1}(I - beta k k^T) + beta v k^T, o_t = S_t q_t regrouped so that the
+// state is read once and written once.
+//
+// The work is a stream: per token a head moves its 64 KiB fp32 state (or 32 KiB bf16) through
+// ~6 flop per element, far below the chip's flop:byte ridge, so no matrix cores are used and
+// the layout exists to keep every HBM access a full, coalesced line:
+//   * state [B][H][D][D], row i (value dim) contiguous over the key dim;
+//   * one workgroup of WAVES wave64s per (b, h); each wave owns D/WAVES consecutive rows and
+//     visits them 4 at a time ("passes"); each 16-lane DPP row of the wave holds one state row,
+//     every lane a fixed slice of E = D/16 columns, loaded as 16-byte vectors, so one load
+//     instruction covers four 256-byte contiguous segments;
+//   * the whole state tile of a wave is loaded into registers before anything else, kept
+//     there across all T tokens of the call, and stored once at the end;
+//   * the per-token vectors (q, k, v, alpha, beta) are staged in LDS once per workgroup,
+//     up to kTokChunk tokens at a time, while the state loads are in flight;
+//   * row dot products S k and S q reduce across the 16 lanes of a row with four DPP steps
+//     (quad_perm 1032, quad_perm 2301, row_half_mirror, row_mirror): every lane ends with the
+//     same total, bit for bit, and no LDS is touched.
+// The fused kernel replaces the staging by the conv (kernel 4) + SiLU + L2-norm + gate
+// prologue of the same page's chain, computed by the workgroup for the 3*D channels its head
+// owns; it is also the only writer of those channels' conv state.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kTokChunk = 8;  // tokens staged in LDS per round
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------------ bf16 <-> fp32
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN (quiet bit set), infinities stay infinite.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float act_to_f32(float x) { return x; }
+__device__ __forceinline__ float act_to_f32(uint16_t x) { return bf16_to_f32(x); }
+template <typename AT> __device__ __forceinline__ AT act_from_f32(float x);
+template <> __device__ __forceinline__ float act_from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t act_from_f32<uint16_t>(float x) {
+    return (uint16_t)f32_to_bf16(x);
+}
+
+// ------------------------------------------------------------------------ DPP reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the same value.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <- 7 - i within each 8 lanes
+    x += dpp_mov<0x140>(x);  // row_mirror: lane i <- 15 - i within the row
+    return x;
+}
+
+// Sum over a whole wave64; the result is wave-uniform.
+__device__ __forceinline__ float wave_sum64(float x) {
+    x = row_sum16(x);
+    const int xi = __builtin_bit_cast(int, x);
+    float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+    float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+    float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+    float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// ------------------------------------------------------------------------ vector memory
+
+template <int NBYTES> struct Words { uint32_t w[(NBYTES + 3) / 4]; };
+
+template <int NBYTES, bool NT>
+__device__ __forceinline__ Words<NBYTES> gload(const void* p) {
+    Words<NBYTES> r;
+    if constexpr (NBYTES == 16) {
+        const u32x4* a = (const u32x4*)p;
+        u32x4 x = NT ? __builtin_nontemporal_load(a) : *a;
+        r.w[0] = x.x; r.w[1] = x.y; r.w[2] = x.z; r.w[3] = x.w;
+    } else if constexpr (NBYTES == 8) {
+        const u32x2* a = (const u32x2*)p;
+        u32x2 x = NT ? __builtin_nontemporal_load(a) : *a;
+        r.w[0] = x.x; r.w[1] = x.y;
+    } else if constexpr (NBYTES == 4) {
+        const uint32_t* a = (const uint32_t*)p;
+        r.w[0] = NT ? __builtin_nontemporal_load(a) : *a;
+    } else {
+        static_assert(NBYTES == 2, "unsupported access width");
+        r.w[0] = *(const uint16_t*)p;
+    }
+    return r;
+}
+
+template <int NBYTES, bool NT>
+__device__ __forceinline__ void gstore(void* p, const Words<NBYTES>& r) {
+    if constexpr (NBYTES == 16) {
+        u32x4 x = {r.w[0], r.w[1], r.w[2], r.w[3]};
+        if (NT) __builtin_nontemporal_store(x, (u32x4*)p); else *(u32x4*)p = x;
+    } else if constexpr (NBYTES == 8) {
+        u32x2 x = {r.w[0], r.w[1]};
+        if (NT) __builtin_nontemporal_store(x, (u32x2*)p); else *(u32x2*)p = x;
+    } else if constexpr (NBYTES == 4) {
+        if (NT) __builtin_nontemporal_store(r.w[0], (uint32_t*)p); else *(uint32_t*)p = r.w[0];
+    } else {
+        static_assert(NBYTES == 2, "unsupported access width");
+        *(uint16_t*)p = (uint16_t)r.w[0];
+    }
+}
+
+// ------------------------------------------------------------------------ tile geometry
+
+template <int D, typename ST, int WAVES>
+struct Geo {
+    static constexpr int E = D / 16;                       // state columns per lane
+    static constexpr int ES = (int)sizeof(ST);             // bytes per state element
+    static constexpr int VW = (E * ES >= 16) ? 16 / ES : E;  // elements per vector access
+    static constexpr int NCH = E / VW;                     // vector accesses per row per lane
+    static constexpr int VB = VW * ES;                     // bytes per vector access
+    static constexpr int NT = 64 * WAVES;                  // threads per workgroup
+    static constexpr int RPW = D / WAVES;                  // rows per wave
+    static constexpr int P = RPW / 4;                      // passes of 4 rows per wave
+    static_assert(D % 16 == 0 && E % VW == 0, "bad head dim");
+    static_assert(RPW % 4 == 0 && P >= 1 && P <= 16, "bad wave count");
+    // Column held by lane l (0..15 within its DPP row) as its element e.
+    static __device__ __forceinline__ int col(int l, int e) {
+        return (e / VW) * (16 * VW) + l * VW + (e % VW);
+    }
+};
+
+template <int D>
+struct TokLds {
+    float q[kTokChunk][D];
+    float k[kTokChunk][D];
+    float v[kTokChunk][D];
+    float alpha[kTokChunk];
+    float beta[kTokChunk];
+    float qf[kTokChunk];  // factor applied to q (scale, times 1/|q| in the fused path)
+    float kf[kTokChunk];  // factor applied to k (1, or 1/|k| in the fused path)
+};
+
+// Load the wave's state rows into registers: S[p][e] = state[row0 + 4p][col(l, e)].
+template <class G, typename ST, bool NT>
+__device__ __forceinline__ void load_state(const ST* __restrict__ Sg, int row0, int l,
+                                           float (&S)[G::P][G::E]) {
+#pragma unroll
+    for (int p = 0; p < G::P; ++p) {
+        const ST* rowp = Sg + (size_t)(row0 + 4 * p) * (G::E * 16);
+#pragma unroll
+        for (int c = 0; c < G::NCH; ++c) {
+            Words<G::VB> w = gload<G::VB, NT>(rowp + c * 16 * G::VW + l * G::VW);
+#pragma unroll
+            for (int e = 0; e < G::VW; ++e) {
+                float x;
+                if constexpr (sizeof(ST) == 4) {
+                    x = __uint_as_float(w.w[e]);
+                } else {
+                    const uint32_t word = w.w[e >> 1];
+                    x = (e & 1) ? __uint_as_float(word & 0xffff0000u) : bf16_to_f32(word & 0xffffu);
+                }
+                S[p][c * G::VW + e] = x;
+            }
+        }
+    }
+}
+
+template <class G, typename ST, bool NT>
+__device__ __forceinline__ void store_state(ST* __restrict__ Sg, int row0, int l,
+                                            const float (&S)[G::P][G::E]) {
+#pragma unroll
+    for (int p = 0; p < G::P; ++p) {
+        ST* rowp = Sg + (size_t)(row0 + 4 * p) * (G::E * 16);
+#pragma unroll
+        for (int c = 0; c < G::NCH; ++c) {
+            Words<G::VB> w;
+            if constexpr (sizeof(ST) == 4) {
+#pragma unroll
+                for (int e = 0; e < G::VW; ++e) w.w[e] = __float_as_uint(S[p][c * G::VW + e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < G::VW; e += 2) {
+                    const uint32_t lo = f32_to_bf16(S[p][c * G::VW + e]);
+                    const uint32_t hi = (e + 1 < G::VW) ? f32_to_bf16(S[p][c * G::VW + e + 1]) : 0u;
+                    w.w[e >> 1] = lo | (hi << 16);
+                }
+            }
+            gstore<G::VB, NT>(rowp + c * 16 * G::VW + l * G::VW, w);
+        }
+    }
+}
+
+// The recurrence for `nt` staged tokens. `obase` points at o[b][t0][h][0]; consecutive tokens
+// are `ostride` elements apart. Row of pass p is row0 + 4p with row0 = wave*RPW + g; the lane
+// with l == p of row group g writes o for that row, so one store covers the wave's rows.
+template <class G, int D, typename AT>
+__device__ __forceinline__ void recur_tokens(float (&S)[G::P][G::E], const TokLds<D>& L, int nt,
+                                             int wave, int g, int l, AT* __restrict__ obase,
+                                             size_t ostride) {
+    const int row0 = wave * G::RPW + g;
+    for (int tt = 0; tt < nt; ++tt) {
+        float kk[G::E], qq[G::E];
+        const float kf = L.kf[tt], qf = L.qf[tt];
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) {
+            kk[e] = L.k[tt][G::col(l, e)] * kf;
+            qq[e] = L.q[tt][G::col(l, e)] * qf;
+        }
+        float kq = 0.f;
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) kq = fmaf(kk[e], qq[e], kq);
+        kq = row_sum16(kq);
+
+        float u[G::P], w[G::P];
+#pragma unroll
+        for (int p = 0; p < G::P; ++p) {
+            float su = 0.f, sw = 0.f;
+#pragma unroll
+            for (int e = 0; e < G::E; ++e) {
+                su = fmaf(S[p][e], kk[e], su);
+                sw = fmaf(S[p][e], qq[e], sw);
+            }
+            u[p] = su;
+            w[p] = sw;
+        }
+#pragma unroll
+        for (int p = 0; p < G::P; ++p) {
+            u[p] = row_sum16(u[p]);
+            w[p] = row_sum16(w[p]);
+        }
+
+        const float a = L.alpha[tt], bt = L.beta[tt];
+        float myo = 0.f;
+#pragma unroll
+        for (int p = 0; p < G::P; ++p) {
+            const float vr = L.v[tt][row0 + 4 * p];
+            const float delta = bt * (vr - a * u[p]);
+#pragma unroll
+            for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(delta, kk[e], a * S[p][e]);
+            const float op = fmaf(a, w[p], delta * kq);
+            myo = (l == p) ? op : myo;
+        }
+        if (l < G::P) obase[(size_t)tt * ostride + wave * G::RPW + 4 * l + g] = act_from_f32<AT>(myo);
+    }
+}
+
+// ------------------------------------------------------------------------ decode kernel
+
+template <int D, typename ST, typename AT, int WAVES, bool NTS>
+__global__ __launch_bounds__(64 * WAVES) void gdn_decode_kernel(
+    int T, int H, const AT* __restrict__ q, const AT* __restrict__ k, const AT* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, ST* __restrict__ state,
+    AT* __restrict__ o, float scale) {
+    using G = Geo<D, ST, WAVES>;
+    __shared__ TokLds<D> L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, l = lane & 15;
+    const int64_t n = blockIdx.x;  // b * H + h
+    const int64_t b = n / H;
+    const int h = (int)(n - b * H);
+    ST* Sg = state + (size_t)n * D * D;
+
+    float S[G::P][G::E];
+    load_state<G, ST, NTS>(Sg, wave * G::RPW + g, l, S);
+
+    for (int t0 = 0; t0 < T; t0 += kTokChunk) {
+        const int nt = min(kTokChunk, T - t0);
+        if (t0 > 0) __syncthreads();  // the previous round's readers are done with L
+        for (int i = tid; i < nt * 3 * D; i += G::NT) {
+            const int tt = i / (3 * D), r = i - tt * 3 * D, which = r / D, j = r - which * D;
+            const size_t tok = ((size_t)b * T + t0 + tt) * H + h;
+            const AT* src = which == 0 ? q : (which == 1 ? k : v);
+            const float x = act_to_f32(src[tok * D + j]);
+            if (which == 0) L.q[tt][j] = x; else if (which == 1) L.k[tt][j] = x; else L.v[tt][j] = x;
+        }
+        if (tid < nt) {
+            const size_t tok = ((size_t)b * T + t0 + tid) * H + h;
+            L.alpha[tid] = alpha[tok];
+            L.beta[tid] = beta[tok];
+            L.qf[tid] = scale;
+            L.kf[tid] = 1.0f;
+        }
+        __syncthreads();
+        recur_tokens<G, D, AT>(S, L, nt, wave, g, l, o + (((size_t)b * T + t0) * H + h) * D,
+                               (size_t)H * D);
+    }
+    store_state<G, ST, NTS>(Sg, wave * G::RPW + g, l, S);
+}
+
+// ------------------------------------------------------------------------ fused kernel
+
+template <int D, typename ST, int WAVES, bool NTS>
+__global__ __launch_bounds__(64 * WAVES) void gdn_conv_gate_decode_kernel(
+    int T, int H, const uint16_t* __restrict__ qkv, uint16_t* __restrict__ conv_state,
+    const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+    const float* __restrict__ a_logit, const float* __restrict__ b_logit, ST* __restrict__ state,
+    uint16_t* __restrict__ o, float scale, float l2_eps) {
+    using G = Geo<D, ST, WAVES>;
+    constexpr int CH = 3 * D;                        // channels owned by this head
+    constexpr int CPT = (CH + G::NT - 1) / G::NT;    // channels per thread
+    __shared__ TokLds<D> L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, l = lane & 15;
+    const int64_t n = blockIdx.x;
+    const int64_t b = n / H;
+    const int h = (int)(n - b * H);
+    const size_t C = (size_t)3 * H * D;
+    ST* Sg = state + (size_t)n * D * D;
+
+    float S[G::P][G::E];
+    load_state<G, ST, NTS>(Sg, wave * G::RPW + g, l, S);
+
+    // Per owned channel: taps, bias, and the rolling window of raw inputs (bf16 bits).
+    float tap[CPT][4], bias[CPT];
+    uint32_t win[CPT][3];
+    size_t chan[CPT];
+#pragma unroll
+    for (int s = 0; s < CPT; ++s) {
+        const int ci = tid + s * G::NT;
+        if (ci < CH) {
+            const int blk = ci / D, j = ci - blk * D;
+            const size_t c = (size_t)blk * H * D + (size_t)h * D + j;
+            chan[s] = c;
+            const float4 w4 = *(const float4*)(conv_w + c * 4);
+            tap[s][0] = w4.x; tap[s][1] = w4.y; tap[s][2] = w4.z; tap[s][3] = w4.w;
+            bias[s] = conv_b ? conv_b[c] : 0.0f;
+            const uint16_t* cs = conv_state + ((size_t)b * C + c) * 3;
+            win[s][0] = cs[0]; win[s][1] = cs[1]; win[s][2] = cs[2];
+        }
+    }
+
+    for (int t0 = 0; t0 < T; t0 += kTokChunk) {
+        const int nt = min(kTokChunk, T - t0);
+        if (t0 > 0) __syncthreads();
+        // Conv (kernel 4, tap 3 on the current input) + SiLU, into LDS.
+#pragma unroll
+        for (int s = 0; s < CPT; ++s) {
+            const int ci = tid + s * G::NT;
+            if (ci < CH) {
+                const int blk = ci / D, j = ci - blk * D;
+                float* dst = blk == 0 ? &L.q[0][j] : (blk == 1 ? &L.k[0][j] : &L.v[0][j]);
+                for (int tt = 0; tt < nt; ++tt) {
+                    const uint32_t x = qkv[((size_t)b * T + t0 + tt) * C + chan[s]];
+                    float y = tap[s][0] * bf16_to_f32(win[s][0]);
+                    y = fmaf(tap[s][1], bf16_to_f32(win[s][1]), y);
+                    y = fmaf(tap[s][2], bf16_to_f32(win[s][2]), y);
+                    y = fmaf(tap[s][3], bf16_to_f32(x), y);
+                    y += bias[s];
+                    win[s][0] = win[s][1]; win[s][1] = win[s][2]; win[s][2] = x;
+                    dst[tt * D] = y / (1.0f + expf(-y));
+                }
+            }
+        }
+        // Gates: beta = sigma(b), alpha = exp(-softplus(a)).
+        if (tid < nt) {
+            const size_t tok = ((size_t)b * T + t0 + tid) * H + h;
+            const float av = a_logit[tok], bv = b_logit[tok];
+            L.beta[tid] = 1.0f / (1.0f + expf(-bv));
+            L.alpha[tid] = expf(-(fmaxf(av, 0.0f) + log1pf(expf(-fabsf(av)))));
+        }
+        __syncthreads();
+        // L2 norms of q and k per token: one wave per (token, q|k) reduction.
+        for (int r = wave; r < 2 * nt; r += WAVES) {
+            const int tt = r >> 1;
+            const float* src = (r & 1) ? L.k[tt] : L.q[tt];
+            float ss = 0.f;
+            for (int j = lane; j < D; j += 64) ss = fmaf(src[j], src[j], ss);
+            ss = wave_sum64(ss);
+            if (lane == 0) {
+                const float inv = 1.0f / sqrtf(ss + l2_eps);
+                if (r & 1) L.kf[tt] = inv; else L.qf[tt] = inv * scale;
+            }
+        }
+        __syncthreads();
+        recur_tokens<G, D, uint16_t>(S, L, nt, wave, g, l,
+                                     o + (((size_t)b * T + t0) * H + h) * D, (size_t)H * D);
+    }
+
+    // The conv state keeps the last three raw inputs, oldest first (a byte-exact move).
+#pragma unroll
+    for (int s = 0; s < CPT; ++s) {
+        const int ci = tid + s * G::NT;
+        if (ci < CH) {
+            uint16_t* cs = conv_state + ((size_t)b * C + chan[s]) * 3;
+            cs[0] = (uint16_t)win[s][0]; cs[1] = (uint16_t)win[s][1]; cs[2] = (uint16_t)win[s][2];
+        }
+    }
+    store_state<G, ST, NTS>(Sg, wave * G::RPW + g, l, S);
+}
+
+// ------------------------------------------------------------------------ dispatch
+
+// Waves per workgroup: 8 passes of 4 rows per wave where the head has enough rows.
+template <int D> constexpr int waves_for() { return D >= 32 ? D / 32 : 1; }
+constexpr bool kNontemporalState = false;
+
+template <int D, typename ST, typename AT>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+    constexpr int W = waves_for<D>();
+    int T = a.T, H = a.H;
+    const AT* q = (const AT*)a.q;
+    const AT* k = (const AT*)a.k;
+    const AT* v = (const AT*)a.v;
+    const float* alpha = a.alpha;
+    const float* beta = a.beta;
+    ST* state = (ST*)a.state;
+    AT* o = (AT*)a.o;
+    float scale = a.scale;
+    void* args[] = {&T, &H, &q, &k, &v, &alpha, &beta, &state, &o, &scale};
+    return hipLaunchKernel((const void*)gdn_decode_kernel<D, ST, AT, W, kNontemporalState>,
+                           dim3((unsigned)(a.B * a.H)), dim3(64 * W), args, 0, s);
+}
+
+template <int D, typename ST>
+hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
+    constexpr int W = waves_for<D>();
+    int T = a.T, H = a.H;
+    const uint16_t* qkv = (const uint16_t*)a.qkv;
+    uint16_t* cs = (uint16_t*)a.conv_state;
+    const float* w = a.conv_w;
+    const float* cb = a.conv_b;
+    const float* al = a.a_logit;
+    const float* bl = a.b_logit;
+    ST* state = (ST*)a.state;
+    uint16_t* o = (uint16_t*)a.o;
+    float scale = a.scale, eps = a.l2_eps;
+    void* args[] = {&T, &H, &qkv, &cs, &w, &cb, &al, &bl, &state, &o, &scale, &eps};
+    return hipLaunchKernel((const void*)gdn_conv_gate_decode_kernel<D, ST, W, kNontemporalState>,
+                           dim3((unsigned)(a.B * a.H)), dim3(64 * W), args, 0, s);
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
+    const bool sf = a.state_dtype == DType::F32, af = a.act == DType::F32;
+    if (sf && af) return launch_decode_t<D, float, float>(a, s);
+    if (sf) return launch_decode_t<D, float, uint16_t>(a, s);
+    if (af) return launch_decode_t<D, uint16_t, float>(a, s);
+    return launch_decode_t<D, uint16_t, uint16_t>(a, s);
+}
+
+template <int D>
+hipError_t launch_fused_d(const FusedArgs& a, hipStream_t s) {
+    if (a.state_dtype == DType::F32) return launch_fused_t<D, float>(a, s);
+    return launch_fused_t<D, uint16_t>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+    switch (a.D) {
+        case 16: return launch_decode_d<16>(a, s);
+        case 32: return launch_decode_d<32>(a, s);
+        case 64: return launch_decode_d<64>(a, s);
+        case 128: return launch_decode_d<128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_conv_gate_decode(const FusedArgs& a, hipStream_t s) {
+    switch (a.D) {
+        case 16: return launch_fused_d<16>(a, s);
+        case 32: return launch_fused_d<32>(a, s);
+        case 64: return launch_fused_d<64>(a, s);
+        case 128: return launch_fused_d<128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn

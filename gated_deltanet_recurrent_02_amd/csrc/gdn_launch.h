@@ -1,0 +1,48 @@
+// Internal interface between the C-ABI layer (gdn_api.cpp) and the kernels (gdn_kernels.hip).
+// Arguments are validated by the caller; the launchers only select a kernel instance and
+// enqueue it on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+struct DecodeArgs {
+    int64_t B;
+    int32_t T, H, D;          // D = dk = dv
+    const void* q;            // act [B][T][H][D]
+    const void* k;            // act [B][T][H][D]
+    const void* v;            // act [B][T][H][D]
+    DType act;
+    const float* alpha;       // [B][T][H]
+    const float* beta;        // [B][T][H]
+    void* state;              // state dtype [B][H][D][D]
+    DType state_dtype;
+    void* o;                  // act [B][T][H][D]
+    float scale;
+};
+
+struct FusedArgs {
+    int64_t B;
+    int32_t T, H, D;
+    const void* qkv;          // bf16 [B][T][3*H*D]
+    void* conv_state;         // bf16 [B][3*H*D][3]
+    const float* conv_w;      // [3*H*D][4]
+    const float* conv_b;      // [3*H*D] or nullptr
+    const float* a_logit;     // [B][T][H]
+    const float* b_logit;     // [B][T][H]
+    void* state;              // state dtype [B][H][D][D]
+    DType state_dtype;
+    void* o;                  // bf16 [B][T][H][D]
+    float scale;
+    float l2_eps;
+};
+
+// Both return hipSuccess or the launch error; nothing is synchronised.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_conv_gate_decode(const FusedArgs& a, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,139 @@
+/*
+ * gdn.h — C ABI of libgdn.so, the MI355X (gfx950) library for the Gated DeltaNet (GDN)
+ * recurrent decode step.
+ *
+ * The operation. For each sequence b and head h the library keeps a state S of dv x dk values
+ * (rows indexed by the value dimension, columns by the key dimension) and, for each of T new
+ * tokens t in order, applies a gated rank-1 delta-rule update and reads the state out:
+ *
+ *     S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t (scale * q_t)
+ *
+ * "GDN tuning limits on Kunlun XPU" (buru.work), section 二 (背景), places this update in every
+ * linear-attention layer (input projection -> short conv, kernel 4 -> gating -> recurrent update
+ * of a 128x128 state per head -> output projection) and describes it as a rank-1 change of the
+ * state plus a decay; the equation above is the gated delta rule, the reading used here.
+ *
+ * Conventions shared by every entry point:
+ *  - Buffers. Every tensor is dense, row-major (last index fastest) and lives in device memory
+ *    of the current HIP device. The caller owns every buffer; the library keeps no pointer
+ *    after a call returns and holds no global state besides a thread-local error string.
+ *  - Alignment. Every device pointer must be 16-byte aligned.
+ *  - Streams. `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *    enqueued asynchronously: no host synchronisation, no allocation, no environment reads.
+ *  - Errors. Arguments are validated on the host before anything is enqueued; on any error
+ *    nothing is enqueued and no buffer changes. Launch failures return GDN_ERR_HIP with the
+ *    HIP error text in gdn_last_error(). A fault inside a kernel surfaces at the caller's next
+ *    synchronisation, as HIP reports it. No call aborts or throws across the ABI.
+ *  - Empty work. B == 0 or T == 0 is a valid no-op (GDN_OK, nothing enqueued); pointers may
+ *    then be NULL.
+ *  - Shapes. dk == dv, one of 16, 32, 64, 128 (others return GDN_ERR_UNSUPPORTED);
+ *    H >= 1; B * H < 2^31.
+ *  - Reentrancy. Calls on different buffers may run concurrently from any threads. Two calls
+ *    that update the same state concurrently race.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, overlapping output */
+    GDN_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head dim, dtype combination) */
+    GDN_ERR_OUT_OF_MEMORY = 3,    /* device allocation failed (gdn_state_alloc only) */
+    GDN_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} gdn_status;
+
+typedef enum {
+    GDN_F32 = 0,  /* IEEE binary32 */
+    GDN_BF16 = 1  /* bfloat16; every bf16 store rounds to nearest even */
+} gdn_dtype;
+
+/*
+ * gdn_state_alloc — allocate a zero-filled recurrent state of B sequences x H heads x dv x dk
+ * elements of `state_dtype` on the current device (the per-head state of the section 二
+ * chain). Synchronous. On success *state_out is a 256-byte aligned device pointer owned by the
+ * caller (release it with gdn_state_free) and *bytes_out (if not NULL) its size in bytes.
+ * Any dense device buffer of the same shape and dtype, e.g. a torch tensor, is an equally valid
+ * state for the step functions.
+ * Errors: GDN_ERR_INVALID_ARGUMENT (B < 1, H < 1, state_out NULL, bad dtype),
+ *         GDN_ERR_UNSUPPORTED (dk != dv or not in {16,32,64,128}),
+ *         GDN_ERR_OUT_OF_MEMORY (hipMalloc failed), GDN_ERR_HIP (other HIP failure).
+ */
+gdn_status gdn_state_alloc(int64_t B, int32_t H, int32_t dk, int32_t dv, gdn_dtype state_dtype,
+                           void** state_out, size_t* bytes_out);
+
+/* gdn_state_free — release a state from gdn_state_alloc (NULL is a no-op). Synchronous. */
+gdn_status gdn_state_free(void* state);
+
+/*
+ * gdn_decode_step — one layer's recurrent step for T sequential tokens of every (b, h); the
+ * operation above ("GDN tuning limits on Kunlun XPU", section 二: the recurrent update that
+ * follows gating). Inputs arrive ready-made: q and k already L2-normalised, alpha and beta
+ * already mapped to gate values.
+ *
+ *   q, k   act_dtype [B][T][H][dk]   read only (may alias each other)
+ *   v      act_dtype [B][T][H][dv]   read only
+ *   alpha  fp32      [B][T][H]       decay, one scalar per (b, t, h)
+ *   beta   fp32      [B][T][H]       write strength, one scalar per (b, t, h)
+ *   state  state_dtype [B][H][dv][dk]  read and updated IN PLACE: S_{t0-1} in, S_{t0+T-1} out
+ *   o      act_dtype [B][T][H][dv]   written: o_t for every token; must not overlap any other
+ *                                    argument (checked by address range)
+ *   scale  multiplies q in the readout (1.0f = the plain definition)
+ *
+ * Arithmetic is fp32 (bf16 inputs widen exactly); a bf16 state is widened on load, kept in fp32
+ * across the T tokens of the call and rounded once when stored.
+ * Errors: GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP (see conventions).
+ */
+gdn_status gdn_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                           const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                           const float* alpha, const float* beta,
+                           void* state, gdn_dtype state_dtype,
+                           void* o, float scale, void* stream);
+
+/*
+ * gdn_conv_gate_decode — the fused layer path of the same chain ("GDN tuning limits on Kunlun
+ * XPU", section 二: short causal conv of kernel size 4, then gating, then the recurrent
+ * update), for T sequential tokens:
+ *   1. causal depthwise conv1d per channel c over (conv_state[c][0..2], x_0[c], x_1[c], ...):
+ *        y_t[c] = sum_{i=0..3} conv_w[c][i] * u[t+i]  (+ conv_b[c]);  tap 3 = current input;
+ *   2. SiLU on every channel, y * sigma(y);
+ *   3. split into q, k, v; q and k scaled to unit length: x / sqrt(sum x^2 + l2_eps);
+ *   4. beta = sigma(b_logit), alpha = exp(-softplus(a_logit));
+ *   5. the recurrent step of gdn_decode_step on those values.
+ *
+ *   qkv        bf16 [B][T][C], C = H*dk + H*dk + H*dv, channel blocks ordered q | k | v, each
+ *              block head-major with the head dimension fastest. Read only.
+ *   conv_state bf16 [B][C][3], the last three raw inputs per channel, oldest first; updated IN
+ *              PLACE to the last three inputs after token T-1 (a byte-exact move of inputs).
+ *   conv_w     fp32 [C][4];  conv_b  fp32 [C] or NULL (no bias)
+ *   a_logit, b_logit  fp32 [B][T][H]
+ *   state      state_dtype [B][H][dv][dk], updated IN PLACE
+ *   o          bf16 [B][T][H][dv], written; must not overlap any other argument
+ * Errors: as gdn_decode_step; conv_state must not overlap state, qkv or o.
+ */
+gdn_status gdn_conv_gate_decode(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                const void* qkv, void* conv_state,
+                                const float* conv_w, const float* conv_b,
+                                const float* a_logit, const float* b_logit,
+                                void* state, gdn_dtype state_dtype,
+                                void* o, float scale, float l2_eps, void* stream);
+
+/* gdn_status_string — static name of a status code ("GDN_OK", ...; "unknown" otherwise). */
+const char* gdn_status_string(gdn_status s);
+
+/* gdn_last_error — detail of the calling thread's most recent failed call ("" if none).
+ * The pointer stays valid until the thread's next library call. */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,94 @@
+"""Helpers for comparing the GPU library with the fp64 oracle (used by the gpu-marked tests).
+
+Error metric: for every (sequence, head), max |X - R| / max |R| over that head's tensor,
+then the maximum over heads, so that a head with small values cannot hide behind a large one.
+Bars (floating point):
+  * fp32 state after all tokens: 1e-4; bf16-stored state: 2e-2 (its own rounding is 2^-8);
+  * fp32 o: 1e-4;
+  * bf16 o: 2e-2 per head, and elementwise |o - R| <= 2^-8 |R| + 1e-4 max|R_head| (one rounding
+    to bf16 of an fp32 value that is itself within ~1e-6 of R).
+Integer/byte work (the conv state, a move of raw bf16 inputs) must match bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import gated_deltanet_recurrent_02_amd as gdn
+import oracle
+
+TOL_STATE = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+TOL_O_F32 = 1e-4
+TOL_O_BF16 = 2e-2
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").double().numpy()
+
+
+def head_rel_err(x: np.ndarray, ref: np.ndarray, nvec: int) -> float:
+    """Max over heads of max|x - ref| / max|ref|; the last `nvec` axes form one head's tensor."""
+    ax = tuple(range(x.ndim - nvec, x.ndim))
+    d = np.abs(x - ref).max(axis=ax)
+    n = np.abs(ref).max(axis=ax)
+    if np.any(np.isnan(d)):
+        return float("inf")
+    return float(np.max(d / np.maximum(n, 1e-300)))
+
+
+def check_state(state_gpu: np.ndarray, ref: np.ndarray, dtype: torch.dtype, what: str = "state"):
+    e = head_rel_err(state_gpu, ref, 2)
+    assert e <= TOL_STATE[dtype], f"{what}: per-head relative error {e:.3e} > {TOL_STATE[dtype]}"
+    return e
+
+
+def check_o(o_gpu: np.ndarray, ref: np.ndarray, dtype: torch.dtype, heads_axis_last: bool = True):
+    """o arrays [..., H, dv] (heads on the second-last axis)."""
+    e = head_rel_err(o_gpu, ref, 1)
+    if dtype == torch.float32:
+        assert e <= TOL_O_F32, f"o: per-head relative error {e:.3e} > {TOL_O_F32}"
+    else:
+        assert e <= TOL_O_BF16, f"o: per-head relative error {e:.3e} > {TOL_O_BF16}"
+        scale = np.abs(ref).max(axis=-1, keepdims=True)
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-4 * scale
+        bad = np.abs(o_gpu - ref) > bound
+        assert not bad.any(), f"o: {int(bad.sum())} elements beyond one bf16 rounding"
+    return e
+
+
+def to_dev(x: dict, dev="cuda") -> dict:
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def gpu_decode(x: dict, scale: float = 1.0):
+    """Run gdn_decode_step on device copies of the inputs; returns (state_after, o) on device."""
+    g = to_dev(x)
+    o = gdn.decode_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state"], scale=scale)
+    torch.cuda.synchronize()
+    return g["state"], o
+
+
+def oracle_decode(x: dict, scale: float = 1.0, heads=None):
+    """Oracle on all heads, or on the listed (b, h) pairs one by one (each pair becomes one
+    sequence with one head). Returns (state [.., D, D], o [.., T, D]) with heads first when
+    sampled, else the full [B,H,..] / [B,T,H,..] arrays."""
+    if heads is None:
+        return oracle.gdn_decode(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["alpha"]),
+                                 f64(x["beta"]), f64(x["state"]), scale=scale)
+    b, h = np.asarray(heads).T
+    bt, ht = torch.as_tensor(b), torch.as_tensor(h)
+    sel = lambda t: t[bt, :, ht]           # [n, T, D] or [n, T]
+    q, k, v = (f64(sel(x[n]))[:, :, None] for n in ("q", "k", "v"))
+    al, be = (f64(sel(x[n]))[:, :, None] for n in ("alpha", "beta"))
+    S0 = f64(x["state"][bt, ht])[:, None]
+    S, o = oracle.gdn_decode(q, k, v, al, be, S0, scale=scale)
+    return S[:, 0], o[:, :, 0]
+
+
+def sample_heads(B: int, H: int, n: int, seed: int = 0):
+    """The first and last head plus n random (b, h) pairs."""
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (B - 1, H - 1)}
+    while len(pairs) < min(n + 2, B * H):
+        pairs.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(pairs)

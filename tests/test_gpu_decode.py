@@ -1,0 +1,225 @@
+"""gdn_decode_step on the GPU against the fp64 oracle (parity), plus invariants and edge cases.
+
+Small shapes are compared element by element over every head; they span several workgroups,
+every head size, both state and activation dtypes, and token counts beyond one LDS round
+(8 tokens) with a ragged tail. The full-size workloads run in the launch configuration the
+benchmark times and are compared on sampled heads computed one by one by the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_recurrent_02_amd as gdn
+import oracle
+from gated_deltanet_recurrent_02_amd import synth
+from parity import (check_o, check_state, f64, gpu_decode, oracle_decode, sample_heads, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def test_tiny_workload_full_compare():
+    x = synth.workload_inputs("decode_b1_h2_d16_t8")
+    _announce("decode_b1_h2_d16_t8")
+    S, o = gpu_decode(x)
+    S_ref, o_ref = oracle_decode(x)
+    check_state(f64(S), S_ref, torch.float32)
+    check_o(f64(o), o_ref, torch.float32)
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,H,T", [(3, 5, 1), (2, 3, 11)])
+def test_small_shapes_full_compare(D, act, sdt, B, H, T):
+    _announce(f"decode B={B} H={H} D={D} T={T} act={act} state={sdt}")
+    x = synth.decode_inputs(B, H, D, T, act=act, state_dtype=sdt, seed=D + T)
+    S, o = gpu_decode(x, scale=0.75)
+    S_ref, o_ref = oracle_decode(x, scale=0.75)
+    check_state(f64(S), S_ref, DT[sdt])
+    check_o(f64(o), o_ref, DT[act])
+
+
+@pytest.mark.parametrize("name,alpha_shift", [
+    ("decode_b1_h48_d128_t1", 2.0), ("decode_b1_h48_d128_t1", -2.0),
+    ("decode_b64_h48_d128_t1", 2.0), ("decode_b256_h48_d128_t1", 2.0)])
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_full_size_workloads_sampled(name, alpha_shift, sdt):
+    _announce(f"{name} alpha_shift={alpha_shift} state={sdt}")
+    x = synth.workload_inputs(name, alpha_shift=alpha_shift, state_dtype=sdt)
+    S, o = gpu_decode(x)
+    heads = sample_heads(x["B"], x["H"], 48, seed=1)
+    S_ref, o_ref = oracle_decode(x, heads=heads)
+    b, h = np.asarray(heads).T
+    check_state(f64(S[b, h]), S_ref, DT[sdt])
+    check_o(f64(o[b, :, h]), o_ref, torch.bfloat16)
+
+
+def test_t4_on_full_heads_fp32_and_bf16():
+    # Multi-token decode at the bottleneck head count, B=8: all heads compared.
+    for sdt in ("f32", "bf16"):
+        _announce(f"decode B=8 H=48 D=128 T=4 state={sdt}")
+        x = synth.decode_inputs(8, 48, 128, 4, state_dtype=sdt, alpha_shift=-2.0, seed=3)
+        S, o = gpu_decode(x)
+        S_ref, o_ref = oracle_decode(x)
+        check_state(f64(S), S_ref, DT[sdt])
+        check_o(f64(o), o_ref, torch.bfloat16)
+
+
+# ------------------------------------------------------------------ invariants
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_identity_gate_leaves_state_bit_identical(sdt):
+    _announce(f"identity gate state={sdt}")
+    x = synth.decode_inputs(4, 6, 128, 3, state_dtype=sdt, seed=4)
+    x["alpha"].fill_(1.0)
+    x["beta"].fill_(0.0)
+    S0 = x["state"].clone()
+    S, o = gpu_decode(x)
+    assert torch.equal(S.cpu().view(torch.int16 if sdt == "bf16" else torch.int32),
+                       S0.view(torch.int16 if sdt == "bf16" else torch.int32))
+    _, o_ref = oracle_decode(x)
+    check_o(f64(o), o_ref, torch.bfloat16)
+
+
+def test_zero_decay_forgets_the_state():
+    _announce("alpha = 0")
+    x = synth.decode_inputs(2, 4, 128, 1, act="f32", seed=5)
+    x["alpha"].zero_()
+    S, o = gpu_decode(x)
+    v, k, be = f64(x["v"])[:, 0], f64(x["k"])[:, 0], f64(x["beta"])[:, 0]
+    ref = be[..., None, None] * v[..., :, None] * k[..., None, :]
+    check_state(f64(S), ref, torch.float32)
+
+
+def test_delta_rule_writes_v_along_unit_k():
+    # alpha = beta = 1 with k = e_j (exact in every dtype): column j of the new state is v.
+    _announce("alpha = beta = 1, k = e_j")
+    x = synth.decode_inputs(2, 4, 64, 1, act="bf16", seed=6)
+    x["alpha"].fill_(1.0)
+    x["beta"].fill_(1.0)
+    k = torch.zeros_like(x["k"])
+    js = [(b * 4 + h) % 64 for b in range(2) for h in range(4)]
+    for i, j in enumerate(js):
+        k[i // 4, 0, i % 4, j] = 1.0
+    x["k"] = k
+    S, _ = gpu_decode(x)
+    S = f64(S)
+    v = f64(x["v"])[:, 0]
+    for i, j in enumerate(js):
+        b, h = divmod(i, 4)
+        err = np.abs(S[b, h, :, j] - v[b, h]).max()
+        assert err <= 2.0 ** -22 * max(1.0, np.abs(v[b, h]).max()), err
+
+
+def test_nan_stays_in_its_head():
+    _announce("NaN isolation")
+    x = synth.decode_inputs(3, 5, 128, 2, seed=7)
+    x["state"][1, 2, 17, 5] = float("nan")
+    S, o = gpu_decode(x)
+    S, o = S.cpu(), o.cpu()
+    bad_s = torch.isnan(S).any(dim=(2, 3))
+    bad_o = torch.isnan(o.float()).any(dim=(1, 3))
+    expect = torch.zeros(3, 5, dtype=torch.bool)
+    expect[1, 2] = True
+    assert torch.equal(bad_s, expect) and torch.equal(bad_o, expect)
+    # within the poisoned head only row 17 is touched
+    rows = torch.isnan(S[1, 2]).any(dim=1)
+    assert rows.nonzero().flatten().tolist() == [17]
+
+
+def test_bitwise_deterministic():
+    _announce("determinism")
+    x = synth.decode_inputs(16, 48, 128, 2, seed=8)
+    S1, o1 = gpu_decode(x)
+    S2, o2 = gpu_decode(x)
+    assert torch.equal(S1, S2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_multi_token_call_equals_single_token_calls():
+    # fp32 state is stored and reloaded exactly, so splitting a call changes no bit.
+    _announce("T=5 vs 5 x T=1 vs 3+2")
+    x = to_dev(synth.decode_inputs(4, 6, 128, 5, seed=9))
+    S_all = x["state"].clone()
+    o_all = gdn.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S_all)
+    S_one = x["state"].clone()
+    outs = []
+    for t in range(5):
+        sl = slice(t, t + 1)
+        outs.append(gdn.decode_step(x["q"][:, sl].contiguous(), x["k"][:, sl].contiguous(),
+                                    x["v"][:, sl].contiguous(), x["alpha"][:, sl].contiguous(),
+                                    x["beta"][:, sl].contiguous(), S_one))
+    S_split = x["state"].clone()
+    o_a = gdn.decode_step(*(x[n][:, :3].contiguous() for n in ("q", "k", "v", "alpha", "beta")), S_split)
+    o_b = gdn.decode_step(*(x[n][:, 3:].contiguous() for n in ("q", "k", "v", "alpha", "beta")), S_split)
+    torch.cuda.synchronize()
+    assert torch.equal(S_all, S_one) and torch.equal(S_all, S_split)
+    o_one = torch.cat(outs, dim=1)
+    assert torch.equal(o_all.view(torch.int16), o_one.view(torch.int16))
+    assert torch.equal(o_all.view(torch.int16), torch.cat([o_a, o_b], 1).view(torch.int16))
+
+
+def test_empty_calls_change_nothing():
+    _announce("B=0 / T=0")
+    x = to_dev(synth.decode_inputs(2, 3, 64, 1, seed=10))
+    S0 = x["state"].clone()
+    e = lambda *s: torch.empty(*s, device="cuda")
+    gdn.decode_step(e(2, 0, 3, 64).bfloat16(), e(2, 0, 3, 64).bfloat16(), e(2, 0, 3, 64).bfloat16(),
+                    e(2, 0, 3), e(2, 0, 3), x["state"])
+    torch.cuda.synchronize()
+    assert torch.equal(S0, x["state"])
+
+
+def test_state_alloc_is_zero_and_usable():
+    _announce("gdn_state_alloc")
+    buf = gdn.state_alloc(3, 4, 64, 64, torch.float32)
+    assert buf.nbytes == 3 * 4 * 64 * 64 * 4 and buf.ptr % 256 == 0
+    S = buf.tensor()
+    assert S.shape == (3, 4, 64, 64) and S.data_ptr() == buf.ptr
+    assert float(S.abs().max()) == 0.0
+    x = synth.decode_inputs(3, 4, 64, 2, seed=11, state_init="zeros")
+    g = to_dev(x)
+    o = gdn.decode_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], S)
+    torch.cuda.synchronize()
+    S_ref, o_ref = oracle_decode(x)
+    check_state(f64(S), S_ref, torch.float32)
+    check_o(f64(o), o_ref, torch.bfloat16)
+    buf16 = gdn.state_alloc(2, 2, 16, 16, torch.bfloat16)
+    assert buf16.nbytes == 2 * 2 * 16 * 16 * 2 and float(buf16.tensor().float().abs().max()) == 0.0
+
+
+def test_state_beyond_4_GiB_offsets():
+    # B=2048 x H=48 fp32 heads = 6.4 GB of state: byte offsets pass 2^32. The state is drawn
+    # on the device from a seeded generator; sampled heads (including the last) are read back
+    # before the call and compared with the oracle one by one.
+    _announce("decode B=2048 H=48 D=128 (6.4 GB state)")
+    B, H, D = 2048, 48, 128
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    state = torch.randn(B, H, D, D, device="cuda", generator=gen).mul_(0.02)
+    rng = np.random.default_rng(12)
+    q = torch.from_numpy(rng.standard_normal((B, 1, H, D)).astype(np.float32))
+    k = torch.from_numpy(rng.standard_normal((B, 1, H, D)).astype(np.float32))
+    q = (q / q.norm(dim=-1, keepdim=True)).bfloat16()
+    k = (k / k.norm(dim=-1, keepdim=True)).bfloat16()
+    v = torch.from_numpy(rng.standard_normal((B, 1, H, D)).astype(np.float32)).bfloat16()
+    alpha = torch.from_numpy(rng.uniform(0.05, 0.95, (B, 1, H)).astype(np.float32))
+    beta = torch.from_numpy(rng.uniform(0.05, 0.95, (B, 1, H)).astype(np.float32))
+    heads = sample_heads(B, H, 24, seed=12) + [(B - 1, 0), (B // 2, H - 1)]
+    b, h = np.asarray(heads).T
+    S0_s = state[torch.as_tensor(b).cuda(), torch.as_tensor(h).cuda()].cpu()
+    o = gdn.decode_step(q.cuda(), k.cuda(), v.cuda(), alpha.cuda(), beta.cuda(), state)
+    torch.cuda.synchronize()
+    S1_s = state[torch.as_tensor(b).cuda(), torch.as_tensor(h).cuda()].cpu()
+    del state
+    sel = lambda t: t[torch.as_tensor(b), :, torch.as_tensor(h)]
+    S_ref, o_ref = oracle.gdn_decode(f64(sel(q))[:, :, None], f64(sel(k))[:, :, None],
+                                     f64(sel(v))[:, :, None], f64(sel(alpha))[:, :, None],
+                                     f64(sel(beta))[:, :, None], f64(S0_s)[:, None])
+    check_state(f64(S1_s), S_ref[:, 0], torch.float32)
+    check_o(f64(o.cpu()[torch.as_tensor(b), :, torch.as_tensor(h)]), o_ref[:, :, 0], torch.bfloat16)

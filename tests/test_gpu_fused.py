@@ -1,0 +1,124 @@
+"""gdn_conv_gate_decode on the GPU against the fp64 oracle.
+
+The conv state is a byte move of raw bf16 inputs and must match bit for bit everywhere; the
+recurrent state and o follow the floating-point bars of parity.py. Small shapes are compared
+over every head; the full-size fused workload (B=256, H=48, D=128, T=4) on sampled heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_recurrent_02_amd as gdn
+import oracle
+from gated_deltanet_recurrent_02_amd import synth
+from parity import check_o, check_state, f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def gpu_fused(x, scale=1.0, l2_eps=1e-6):
+    g = to_dev(x)
+    o = gdn.conv_gate_decode(g["qkv"], g["conv_state"], g["conv_w"], g["conv_b"], g["a_logit"],
+                             g["b_logit"], g["state"], scale=scale, l2_eps=l2_eps)
+    torch.cuda.synchronize()
+    return g["state"], o, g["conv_state"]
+
+
+def oracle_fused(x, scale=1.0, l2_eps=1e-6):
+    H, D = x["H"], x["D"]
+    cb = None if x["conv_b"] is None else f64(x["conv_b"])
+    return oracle.gdn_conv_gate_decode(f64(x["qkv"]), f64(x["conv_state"]), f64(x["conv_w"]), cb,
+                                       f64(x["a_logit"]), f64(x["b_logit"]), f64(x["state"]),
+                                       H=H, dk=D, dv=D, scale=scale, l2_eps=l2_eps)
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,H,T,bias", [(3, 5, 1, False), (2, 3, 4, True), (2, 2, 11, False)])
+def test_small_shapes_full_compare(D, sdt, B, H, T, bias):
+    _announce(f"fused B={B} H={H} D={D} T={T} state={sdt} bias={bias}")
+    x = synth.fused_inputs(B, H, D, T, state_dtype=sdt, with_bias=bias, seed=D * 7 + T)
+    S, o, cs = gpu_fused(x, scale=0.5)
+    S_ref, o_ref, cs_ref = oracle_fused(x, scale=0.5)
+    assert np.array_equal(f64(cs), cs_ref)
+    check_state(f64(S), S_ref, DT[sdt])
+    check_o(f64(o), o_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_full_size_fused_workload_sampled(sdt):
+    _announce(f"fused_b256_h48_d128_t4 state={sdt}")
+    x = synth.workload_inputs("fused_b256_h48_d128_t4", state_dtype=sdt)
+    S0 = x["state"]
+    S, o, cs = gpu_fused(x)
+    B, H, D, T = x["B"], x["H"], x["D"], x["T"]
+    # Conv state: every byte, against the oracle's prologue over the whole batch.
+    q, k, v, al, be, cs_ref = oracle.conv_gate(f64(x["qkv"]), f64(x["conv_state"]),
+                                               f64(x["conv_w"]), None, f64(x["a_logit"]),
+                                               f64(x["b_logit"]), H, D, D)
+    assert np.array_equal(f64(cs), cs_ref)
+    # Recurrent state and o: sampled sequences, the oracle's fused path one sequence at a time.
+    rng = np.random.default_rng(2)
+    seqs = sorted({0, B - 1, *rng.integers(0, B, 6).tolist()})
+    for b in seqs:
+        xb = dict(qkv=x["qkv"][b:b + 1], conv_state=x["conv_state"][b:b + 1], conv_w=x["conv_w"],
+                  conv_b=None, a_logit=x["a_logit"][b:b + 1], b_logit=x["b_logit"][b:b + 1],
+                  state=S0[b:b + 1], H=H, D=D)
+        S_ref, o_ref, _ = oracle_fused(xb)
+        check_state(f64(S[b:b + 1]), S_ref, DT[sdt], what=f"state of sequence {b}")
+        check_o(f64(o[b:b + 1]), o_ref, torch.bfloat16)
+
+
+def test_fused_equals_prologue_then_decode_step():
+    # The fused kernel against the decode kernel fed with the oracle's prologue outputs
+    # (rounded to fp32): same state to fp32 accuracy.
+    _announce("fused vs oracle prologue + decode kernel")
+    x = synth.fused_inputs(4, 6, 128, 3, seed=21)
+    S_f, o_f, _ = gpu_fused(x)
+    q, k, v, al, be, _ = oracle.conv_gate(f64(x["qkv"]), f64(x["conv_state"]), f64(x["conv_w"]),
+                                          None, f64(x["a_logit"]), f64(x["b_logit"]), 6, 128, 128)
+    t = lambda a: torch.from_numpy(a.astype(np.float32)).cuda()
+    S_d = x["state"].cuda()
+    o_d = gdn.decode_step(t(q), t(k), t(v), t(al), t(be), S_d)
+    torch.cuda.synchronize()
+    check_state(f64(S_f), f64(S_d), torch.float32)
+
+
+def test_identity_taps_and_zero_logit_gates():
+    # Taps (0,0,0,1): v is SiLU of the current input. Logits 0: alpha = beta = 1/2.
+    _announce("fused identity taps")
+    x = synth.fused_inputs(2, 3, 64, 2, seed=22)
+    x["conv_w"].zero_()
+    x["conv_w"][:, 3] = 1.0
+    x["a_logit"].zero_()
+    x["b_logit"].zero_()
+    S, o, cs = gpu_fused(x)
+    S_ref, o_ref, cs_ref = oracle_fused(x)
+    assert np.array_equal(f64(cs), cs_ref)
+    check_state(f64(S), S_ref, torch.float32)
+    check_o(f64(o), o_ref, torch.bfloat16)
+
+
+def test_conv_state_roll_for_short_calls():
+    # T = 1 and 2 take the oldest entries of the new conv state from the old one.
+    for T in (1, 2):
+        _announce(f"fused conv-state roll T={T}")
+        x = synth.fused_inputs(3, 2, 32, T, seed=23 + T)
+        _, _, cs = gpu_fused(x)
+        seq = torch.cat([x["conv_state"], x["qkv"].transpose(1, 2)], dim=2)
+        assert torch.equal(cs.cpu().view(torch.int16), seq[:, :, -3:].contiguous().view(torch.int16))
+
+
+def test_fused_deterministic():
+    _announce("fused determinism")
+    x = synth.fused_inputs(8, 48, 128, 4, seed=24)
+    a = gpu_fused(x)
+    b = gpu_fused(x)
+    for u, w in zip(a, b):
+        assert torch.equal(u.view(torch.int16), w.view(torch.int16))
