@@ -12,19 +12,24 @@
 // the layout exists to keep every HBM access a full, coalesced line:
 //   * state [B][H][D][D], row i (value dim) contiguous over the key dim;
 //   * SPLIT workgroups of WAVES wave64s per (b, h); each wave owns consecutive rows and visits
-//     them 4 at a time ("passes"); each 16-lane DPP row of the wave holds one state row, every
-//     lane a fixed slice of E = D/16 columns, loaded as 16-byte vectors, so one load
-//     instruction covers four 256-byte contiguous segments;
-//   * the whole state tile of a wave is loaded into registers before anything else, kept
-//     there across all T tokens of the call, and stored once at the end;
-//   * the per-token vectors (q, k, v, alpha, beta) are staged in LDS once per workgroup,
-//     up to TCH tokens at a time, while the state loads are in flight;
-//   * row dot products S k and S q reduce across the 16 lanes of a row with four DPP steps
-//     (quad_perm 1032, quad_perm 2301, row_half_mirror, row_mirror): every lane ends with the
-//     same total, bit for bit, and no LDS is touched.
+//     them RPP = 64/LPR at a time ("passes"); LPR lanes hold one state row, every lane a fixed
+//     slice of E = D/LPR columns loaded as 16-byte vectors, so a load instruction covers RPP
+//     row segments of LPR*16 bytes each (whole 128-byte lines or more);
+//   * the whole state tile of a wave is loaded into registers before anything else, kept there
+//     across all T tokens of the call, and stored once at the end;
+//   * the per-token vectors (q, k, v, alpha, beta) are staged in LDS once per workgroup, up to
+//     TCH tokens at a time, while the state loads are in flight;
+//   * row dot products S k and S q reduce across the LPR lanes of a row with DPP steps
+//     (quad_perm 1032, quad_perm 2301, then row_half_mirror and row_mirror as LPR needs):
+//     every lane ends with the same total, bit for bit, and no LDS is touched.
+// Per-head scalars are folded instead of scaling vectors: k and q stay raw in LDS and their
+// factors (1/|k|, scale/|q| in the fused path) multiply the row totals. For several tokens the
+// registers hold S' = S / c with c the running product of alpha over the call's tokens, which
+// turns the update into one FMA per element (S' += (delta / c) k); c is folded back before the
+// store, or earlier if it leaves [2^-64, 2^64] (see token_step).
 // The fused kernel replaces the staging by the conv (kernel 4) + SiLU + L2-norm + gate
-// prologue of the same page's chain, computed by the workgroup for the 3*D channels its head
-// owns; it is also the only writer of those channels' conv state.
+// prologue of the same chain, computed by the workgroup for the 3*D channels its head owns; it
+// is also the only reader and writer of those channels' conv state.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,12 +48,22 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// Round to nearest, ties to even; NaN stays NaN (quiet bit set), infinities stay infinite.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to two bf16 (lo in bits 0-15), round to nearest even, NaN stays NaN: gfx950's
+// v_cvt_pk_bf16_f32, whose results were checked against the bit-level definition
+// (u + 0x7fff + ((u >> 16) & 1)) >> 16, with NaN -> (u >> 16) | 0x40, on all 2^32 inputs.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return f32x2_to_bf16x2(f, 0.0f) & 0xffffu; }
+
+// A value every lane of the wave holds identically, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
 __device__ __forceinline__ float act_to_f32(float x) { return x; }
@@ -67,18 +82,21 @@ __device__ __forceinline__ float dpp_mov(float x) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 16 lanes of a DPP row; every lane of the row receives the same value.
-__device__ __forceinline__ float row_sum16(float x) {
-    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-    x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <- 7 - i within each 8 lanes
-    x += dpp_mov<0x140>(x);  // row_mirror: lane i <- 15 - i within the row
+// Sum over aligned groups of LPR lanes (4, 8 or 16); every lane of a group receives the same
+// value.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "groups of 4, 8 or 16 lanes");
+    x += dpp_mov<0xB1>(x);                           // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp_mov<0x4E>(x);                           // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPR >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: i <- 7 - i in 8 lanes
+    if constexpr (LPR >= 16) x += dpp_mov<0x140>(x); // row_mirror: i <- 15 - i in 16 lanes
     return x;
 }
 
 // Sum over a whole wave64; the result is wave-uniform.
 __device__ __forceinline__ float wave_sum64(float x) {
-    x = row_sum16(x);
+    x = row_sum<16>(x);
     const int xi = __builtin_bit_cast(int, x);
     float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
     float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
@@ -132,68 +150,82 @@ __device__ __forceinline__ void gstore(void* p, const Words<NBYTES>& r) {
 
 // A kernel instance: head dim D, state type ST, WAVES wave64s per workgroup, SPLIT workgroups
 // per head (each owning D/SPLIT consecutive rows), TCH tokens staged in LDS per round,
-// nontemporal state loads (NTL) / stores (NTS), and XCD-contiguous tile order (XCD).
+// nontemporal state loads (NTL) / stores (NTS), the tile order over XCDs (XCD, see
+// tile_index), and LPR lanes per state row.
 template <int D_, typename ST_, int WAVES_, int SPLIT_, int TCH_, bool NTL_, bool NTS_,
-          bool XCD_ = false>
+          int XCD_ = 0, int LPR_ = 16>
 struct Geo {
     static constexpr int D = D_;
     using ST = ST_;
-    static constexpr int WAVES = WAVES_, SPLIT = SPLIT_, TCH = TCH_;
-    static constexpr bool NTL = NTL_, NTS = NTS_, XCD = XCD_;
-    static constexpr int E = D / 16;                         // state columns per lane
+    static constexpr int WAVES = WAVES_, SPLIT = SPLIT_, TCH = TCH_, XCD = XCD_, LPR = LPR_;
+    static constexpr bool NTL = NTL_, NTS = NTS_;
+    static constexpr int E = D / LPR;                        // state columns per lane
     static constexpr int ES = (int)sizeof(ST);               // bytes per state element
     static constexpr int VW = (E * ES >= 16) ? 16 / ES : E;  // elements per vector access
     static constexpr int NCH = E / VW;                       // vector accesses per row per lane
     static constexpr int VB = VW * ES;                       // bytes per vector access
     static constexpr int NT = 64 * WAVES;                    // threads per workgroup
+    static constexpr int RPP = 64 / LPR;                     // rows per pass of a wave
     static constexpr int RPG = D / SPLIT;                    // rows per workgroup
     static constexpr int RPW = RPG / WAVES;                  // rows per wave
-    static constexpr int P = RPW / 4;                        // passes of 4 rows per wave
-    static_assert(D % 16 == 0 && E % VW == 0, "bad head dim");
+    static constexpr int P = RPW / RPP;                      // passes per wave
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "lanes per row");
+    static_assert(D % LPR == 0 && E >= 1 && E % VW == 0, "bad head dim");
     static_assert(D % SPLIT == 0 && RPG % WAVES == 0, "bad split");
-    static_assert(RPW % 4 == 0 && P >= 1 && P <= 16, "bad wave count");
+    static_assert(RPW % RPP == 0 && P >= 1 && P <= LPR, "bad wave count");
     static_assert(TCH >= 1, "bad token chunk");
-    // Column held by lane l (0..15 within its DPP row) as its element e.
+    // Column held by lane l (0..LPR-1 within its row group) as its element e.
     static __device__ __forceinline__ int col(int l, int e) {
-        return (e / VW) * (16 * VW) + l * VW + (e % VW);
+        return (e / VW) * (LPR * VW) + l * VW + (e % VW);
     }
 };
 
-// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8). With
-// XCD set, tile indices are renumbered so that each XCD walks one contiguous range of tiles;
-// the map is a bijection of [0, n) for any n.
-template <bool XCD>
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8), and
+// each XCD has its own L2. The tile order decides which tiles share an L2:
+//   XCD 0: tile = workgroup index (consecutive tiles on different XCDs);
+//   XCD 1: each XCD walks one contiguous range of tiles;
+//   XCD 2: the SPLIT tiles of a head stay on one XCD (its q, k, v are fetched into one L2),
+//          consecutive heads go to consecutive XCDs; heads past the last multiple of 8 keep
+//          the plain order.
+// Each map is a bijection of [0, n) for n = gridDim.x.
+template <int XCD, int SPLIT>
 __device__ __forceinline__ uint32_t tile_index(uint32_t bid, uint32_t n) {
-    if constexpr (!XCD) {
-        return bid;
-    } else {
+    if constexpr (XCD == 1) {
         const uint32_t x = bid & 7u, i = bid >> 3, q = n >> 3, r = n & 7u;
         return x * q + min(x, r) + i;
+    } else if constexpr (XCD == 2) {
+        const uint32_t grouped = (n / (8u * SPLIT)) * (8u * SPLIT);
+        if (bid >= grouped) return bid;
+        const uint32_t x = bid & 7u, i = bid >> 3;
+        return ((i / SPLIT) * 8u + x) * SPLIT + (i % SPLIT);
+    } else {
+        return bid;
     }
 }
 
+// Per-token vectors of one head, raw (k and q unscaled), and the per-token scalars.
 template <int D, int TCH>
 struct TokLds {
-    float q[TCH][D];
-    float k[TCH][D];
-    float v[TCH][D];
+    alignas(16) float q[TCH][D];
+    alignas(16) float k[TCH][D];
+    alignas(16) float v[TCH][D];
     float alpha[TCH];
     float beta[TCH];
-    float qf[TCH];  // factor applied to q (scale, times 1/|q| in the fused path)
-    float kf[TCH];  // factor applied to k (1, or 1/|k| in the fused path)
+    float qf[TCH];  // factor of q in the readout: scale (times 1/|q| in the fused path)
+    float kf[TCH];  // factor of k: 1 (or 1/|k| in the fused path)
 };
 
-// Load the wave's state rows into registers: S[p][e] = state[row0 + 4p][col(l, e)].
+// Load the wave's state rows into registers: S[p][e] = state[row0 + p*RPP][col(l, e)].
 template <class G>
 __device__ __forceinline__ void load_state(const typename G::ST* __restrict__ Sg, int row0, int l,
                                            float (&S)[G::P][G::E]) {
     using ST = typename G::ST;
 #pragma unroll
     for (int p = 0; p < G::P; ++p) {
-        const ST* rowp = Sg + (size_t)(row0 + 4 * p) * G::D;
+        const ST* rowp = Sg + (size_t)(row0 + p * G::RPP) * G::D;
 #pragma unroll
         for (int c = 0; c < G::NCH; ++c) {
-            Words<G::VB> w = gload<G::VB, G::NTL>(rowp + c * 16 * G::VW + l * G::VW);
+            Words<G::VB> w = gload<G::VB, G::NTL>(rowp + c * G::LPR * G::VW + l * G::VW);
 #pragma unroll
             for (int e = 0; e < G::VW; ++e) {
                 float x;
@@ -215,7 +247,7 @@ __device__ __forceinline__ void store_state(typename G::ST* __restrict__ Sg, int
     using ST = typename G::ST;
 #pragma unroll
     for (int p = 0; p < G::P; ++p) {
-        ST* rowp = Sg + (size_t)(row0 + 4 * p) * G::D;
+        ST* rowp = Sg + (size_t)(row0 + p * G::RPP) * G::D;
 #pragma unroll
         for (int c = 0; c < G::NCH; ++c) {
             Words<G::VB> w;
@@ -225,74 +257,184 @@ __device__ __forceinline__ void store_state(typename G::ST* __restrict__ Sg, int
             } else {
 #pragma unroll
                 for (int e = 0; e < G::VW; e += 2) {
-                    const uint32_t lo = f32_to_bf16(S[p][c * G::VW + e]);
-                    const uint32_t hi = (e + 1 < G::VW) ? f32_to_bf16(S[p][c * G::VW + e + 1]) : 0u;
-                    w.w[e >> 1] = lo | (hi << 16);
+                    const float hi = (e + 1 < G::VW) ? S[p][c * G::VW + e + 1] : 0.0f;
+                    w.w[e >> 1] = f32x2_to_bf16x2(S[p][c * G::VW + e], hi);
                 }
             }
-            gstore<G::VB, G::NTS>(rowp + c * 16 * G::VW + l * G::VW, w);
+            gstore<G::VB, G::NTS>(rowp + c * G::LPR * G::VW + l * G::VW, w);
         }
     }
 }
 
-// The recurrence for `nt` staged tokens. `obase` points at o[b][t0][h][0]; consecutive tokens
-// are `ostride` elements apart. The row of pass p is row0 + 4p with row0 = rbase + g, rbase
-// the wave's first row; the lane with l == p of row group g writes o for that row, so one
-// store covers all the wave's rows.
-template <class G, typename AT>
-__device__ __forceinline__ void recur_tokens(float (&S)[G::P][G::E],
-                                             const TokLds<G::D, G::TCH>& L, int nt, int rbase,
-                                             int g, int l, AT* __restrict__ obase, size_t ostride) {
-    const int row0 = rbase + g;
-    for (int tt = 0; tt < nt; ++tt) {
-        float kk[G::E], qq[G::E];
-        const float kf = L.kf[tt], qf = L.qf[tt];
+// ------------------------------------------------------------------------ one token
+
+// Row totals shared by both token forms: kq = k_raw . q_raw and, per pass, u = S k_raw and
+// w = S q_raw (S as held in registers), reduced over the row's lanes.
+template <class G>
+__device__ __forceinline__ float row_dots(const float (&S)[G::P][G::E], const float (&kk)[G::E],
+                                          const float (&qq)[G::E], float (&u)[G::P],
+                                          float (&w)[G::P]) {
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) kq = fmaf(kk[e], qq[e], kq);
+#pragma unroll
+    for (int p = 0; p < G::P; ++p) {
+        float su = 0.f, sw = 0.f;
 #pragma unroll
         for (int e = 0; e < G::E; ++e) {
-            kk[e] = L.k[tt][G::col(l, e)] * kf;
-            qq[e] = L.q[tt][G::col(l, e)] * qf;
+            su = fmaf(S[p][e], kk[e], su);
+            sw = fmaf(S[p][e], qq[e], sw);
         }
-        float kq = 0.f;
+        u[p] = su;
+        w[p] = sw;
+    }
+    kq = row_sum<G::LPR>(kq);
 #pragma unroll
-        for (int e = 0; e < G::E; ++e) kq = fmaf(kk[e], qq[e], kq);
-        kq = row_sum16(kq);
+    for (int p = 0; p < G::P; ++p) {
+        u[p] = row_sum<G::LPR>(u[p]);
+        w[p] = row_sum<G::LPR>(w[p]);
+    }
+    return kq;
+}
 
-        float u[G::P], w[G::P];
+// One token with S held as is. k = kf k_raw, q = qf q_raw:
+//   u = kf (S k_raw);  delta = beta (v - alpha u);  S <- alpha S + (delta kf) k_raw;
+//   o = qf (alpha (S q_raw) + (delta kf) (k_raw . q_raw)).
+// Returns, on the lane with l == p of each row group, o of the row of pass p.
+template <class G>
+__device__ __forceinline__ float token_plain(float (&S)[G::P][G::E], const float (&kk)[G::E],
+                                             const float (&qq)[G::E], const float (&vr)[G::P],
+                                             float a, float bt, float kf, float qf, int l) {
+    float u[G::P], w[G::P];
+    const float kq = row_dots<G>(S, kk, qq, u, w);
+    float myo = 0.f;
 #pragma unroll
-        for (int p = 0; p < G::P; ++p) {
-            float su = 0.f, sw = 0.f;
+    for (int p = 0; p < G::P; ++p) {
+        const float delta = bt * (vr[p] - a * (kf * u[p]));
+        const float dk = delta * kf;
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(dk, kk[e], a * S[p][e]);
+        const float op = qf * fmaf(a, w[p], dk * kq);
+        myo = (l == p) ? op : myo;
+    }
+    return myo;
+}
+
+// One token with registers holding S' = S / c; cn = c alpha (in [2^-64, 2^64]) is the new
+// scale. With u' = S' k_raw, w' = S' q_raw:
+//   delta = beta (v - alpha kf c u');  S' <- S' + (delta kf / cn) k_raw;
+//   o = qf (cn w' + (delta kf) (k_raw . q_raw)),
+// since alpha S + dk k = cn (S' + dk k / cn) and alpha S q = cn S' q: one FMA per element.
+template <class G>
+__device__ __forceinline__ float token_scaled(float (&S)[G::P][G::E], const float (&kk)[G::E],
+                                              const float (&qq)[G::E], const float (&vr)[G::P],
+                                              float a, float bt, float kf, float qf, float c,
+                                              float cn, int l) {
+    float u[G::P], w[G::P];
+    const float kq = row_dots<G>(S, kk, qq, u, w);
+    const float kc = kf * c, inv_cn = __builtin_amdgcn_rcpf(cn);
+    float myo = 0.f;
+#pragma unroll
+    for (int p = 0; p < G::P; ++p) {
+        const float delta = bt * (vr[p] - a * (kc * u[p]));
+        const float dk = delta * kf;
+        const float coef = dk * inv_cn;
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(coef, kk[e], S[p][e]);
+        const float op = qf * fmaf(cn, w[p], dk * kq);
+        myo = (l == p) ? op : myo;
+    }
+    return myo;
+}
+
+template <class G>
+__device__ __forceinline__ void scale_state(float (&S)[G::P][G::E], float c) {
+#pragma unroll
+    for (int p = 0; p < G::P; ++p)
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) S[p][e] *= c;
+}
+
+// Per-token operands of a lane: its E columns of raw k and q, the v entries of its rows, and
+// the token's scalars (wave-uniform, moved to scalar registers).
+template <class G>
+struct TokenOperands {
+    float kk[G::E], qq[G::E], vr[G::P];
+    float a, bt, kf, qf;
+    __device__ __forceinline__ void load(const TokLds<G::D, G::TCH>& L, int tt, int row0, int l) {
+        if constexpr (G::VW % 4 == 0) {
+            // columns e..e+3 of a lane are contiguous and 16-byte aligned: ds_read_b128
+#pragma unroll
+            for (int e = 0; e < G::E; e += 4) {
+                const float4 k4 = *(const float4*)&L.k[tt][G::col(l, e)];
+                const float4 q4 = *(const float4*)&L.q[tt][G::col(l, e)];
+                kk[e] = k4.x; kk[e + 1] = k4.y; kk[e + 2] = k4.z; kk[e + 3] = k4.w;
+                qq[e] = q4.x; qq[e + 1] = q4.y; qq[e + 2] = q4.z; qq[e + 3] = q4.w;
+            }
+        } else {
 #pragma unroll
             for (int e = 0; e < G::E; ++e) {
-                su = fmaf(S[p][e], kk[e], su);
-                sw = fmaf(S[p][e], qq[e], sw);
+                kk[e] = L.k[tt][G::col(l, e)];
+                qq[e] = L.q[tt][G::col(l, e)];
             }
-            u[p] = su;
-            w[p] = sw;
         }
 #pragma unroll
-        for (int p = 0; p < G::P; ++p) {
-            u[p] = row_sum16(u[p]);
-            w[p] = row_sum16(w[p]);
-        }
+        for (int p = 0; p < G::P; ++p) vr[p] = L.v[tt][row0 + p * G::RPP];
+        a = uniform(L.alpha[tt]);
+        bt = uniform(L.beta[tt]);
+        kf = uniform(L.kf[tt]);
+        qf = uniform(L.qf[tt]);
+    }
+};
 
-        const float a = L.alpha[tt], bt = L.beta[tt];
-        float myo = 0.f;
-#pragma unroll
-        for (int p = 0; p < G::P; ++p) {
-            const float vr = L.v[tt][row0 + 4 * p];
-            const float delta = bt * (vr - a * u[p]);
-#pragma unroll
-            for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(delta, kk[e], a * S[p][e]);
-            const float op = fmaf(a, w[p], delta * kq);
-            myo = (l == p) ? op : myo;
+// The recurrence for `nt` staged tokens. `obase` points at o[b][t0][h][0]; consecutive tokens
+// are `ostride` elements apart. The row of pass p is row0 + p*RPP with row0 = rbase + g, rbase
+// the wave's first row; the lane with l == p of row group g writes o for that row, so one
+// store covers all the wave's rows.
+// With MULTI the registers hold S / c and `c` carries the scale across rounds: tokens run in
+// the scaled form while c alpha stays in [2^-64, 2^64]; a token that would leave that range
+// (alpha = 0, very small or large, NaN) folds c back into the registers and runs plainly.
+template <class G, bool MULTI, typename AT>
+__device__ __forceinline__ void recur_tokens(float (&S)[G::P][G::E],
+                                             const TokLds<G::D, G::TCH>& L, int nt, int rbase,
+                                             int g, int l, AT* __restrict__ obase, size_t ostride,
+                                             float& c) {
+    const int row0 = rbase + g;
+    auto put_o = [&](int tt, float myo) {
+        if (l < G::P) obase[(size_t)tt * ostride + rbase + l * G::RPP + g] = act_from_f32<AT>(myo);
+    };
+    if constexpr (!MULTI) {
+        for (int tt = 0; tt < nt; ++tt) {
+            TokenOperands<G> t;
+            t.load(L, tt, row0, l);
+            put_o(tt, token_plain<G>(S, t.kk, t.qq, t.vr, t.a, t.bt, t.kf, t.qf, l));
         }
-        if (l < G::P) obase[(size_t)tt * ostride + rbase + 4 * l + g] = act_from_f32<AT>(myo);
+    } else {
+        int tt = 0;
+        while (tt < nt) {
+            for (; tt < nt; ++tt) {
+                TokenOperands<G> t;
+                t.load(L, tt, row0, l);
+                const float cn = c * t.a;
+                if (!(cn >= 0x1p-64f && cn <= 0x1p64f)) break;
+                put_o(tt, token_scaled<G>(S, t.kk, t.qq, t.vr, t.a, t.bt, t.kf, t.qf, c, cn, l));
+                c = cn;
+            }
+            if (tt < nt) {
+                TokenOperands<G> t;
+                t.load(L, tt, row0, l);
+                if (c != 1.0f) scale_state<G>(S, c);
+                c = 1.0f;
+                put_o(tt, token_plain<G>(S, t.kk, t.qq, t.vr, t.a, t.bt, t.kf, t.qf, l));
+                ++tt;
+            }
+        }
     }
 }
 
 // ------------------------------------------------------------------------ decode kernel
 
-template <class G, typename AT>
+template <class G, bool MULTI, typename AT>
 __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     int T, int H, const AT* __restrict__ q, const AT* __restrict__ k, const AT* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -300,8 +442,8 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     constexpr int D = G::D;
     __shared__ TokLds<D, G::TCH> L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, l = lane & 15;
-    const uint32_t tile = tile_index<G::XCD>(blockIdx.x, gridDim.x);
+    const int g = lane / G::LPR, l = lane % G::LPR;
+    const uint32_t tile = tile_index<G::XCD, G::SPLIT>(blockIdx.x, gridDim.x);
     const int64_t n = tile / G::SPLIT;  // b * H + h
     const int part = (int)(tile - n * G::SPLIT);
     const int64_t b = n / H;
@@ -312,6 +454,7 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     float S[G::P][G::E];
     load_state<G>(Sg, rbase + g, l, S);
 
+    float c = 1.0f;
     for (int t0 = 0; t0 < T; t0 += G::TCH) {
         const int nt = min(G::TCH, T - t0);
         if (t0 > 0) __syncthreads();  // the previous round's readers are done with L
@@ -330,9 +473,10 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
             L.kf[tid] = 1.0f;
         }
         __syncthreads();
-        recur_tokens<G, AT>(S, L, nt, rbase, g, l, o + (((size_t)b * T + t0) * H + h) * D,
-                            (size_t)H * D);
+        recur_tokens<G, MULTI, AT>(S, L, nt, rbase, g, l, o + (((size_t)b * T + t0) * H + h) * D,
+                                   (size_t)H * D, c);
     }
+    if (MULTI && c != 1.0f) scale_state<G>(S, c);
     store_state<G>(Sg, rbase + g, l, S);
 }
 
@@ -340,7 +484,7 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
 
 // One workgroup per head (SPLIT == 1): it is then the only reader and writer of the head's
 // conv-state channels.
-template <class G>
+template <class G, bool MULTI>
 __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
     int T, int H, const uint16_t* __restrict__ qkv, uint16_t* __restrict__ conv_state,
     const float* __restrict__ conv_w, const float* __restrict__ conv_b,
@@ -352,8 +496,9 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
     constexpr int CPT = (CH + G::NT - 1) / G::NT;    // channels per thread
     __shared__ TokLds<D, G::TCH> L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, l = lane & 15;
-    const int64_t n = blockIdx.x;
+    const int g = lane / G::LPR, l = lane % G::LPR;
+    const uint32_t tile = tile_index<G::XCD, 1>(blockIdx.x, gridDim.x);
+    const int64_t n = tile;
     const int64_t b = n / H;
     const int h = (int)(n - b * H);
     const size_t C = (size_t)3 * H * D;
@@ -382,6 +527,7 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
         }
     }
 
+    float c = 1.0f;
     for (int t0 = 0; t0 < T; t0 += G::TCH) {
         const int nt = min(G::TCH, T - t0);
         if (t0 > 0) __syncthreads();
@@ -425,8 +571,8 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
             }
         }
         __syncthreads();
-        recur_tokens<G, uint16_t>(S, L, nt, rbase, g, l, o + (((size_t)b * T + t0) * H + h) * D,
-                                  (size_t)H * D);
+        recur_tokens<G, MULTI, uint16_t>(S, L, nt, rbase, g, l,
+                                         o + (((size_t)b * T + t0) * H + h) * D, (size_t)H * D, c);
     }
 
     // The conv state keeps the last three raw inputs, oldest first (a byte-exact move).
@@ -438,12 +584,13 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
             cs[0] = (uint16_t)win[s][0]; cs[1] = (uint16_t)win[s][1]; cs[2] = (uint16_t)win[s][2];
         }
     }
+    if (MULTI && c != 1.0f) scale_state<G>(S, c);
     store_state<G>(Sg, rbase + g, l, S);
 }
 
 // ------------------------------------------------------------------------ dispatch
 
-template <class G, typename AT>
+template <class G, bool MULTI, typename AT>
 hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
     int T = a.T, H = a.H;
     const AT* q = (const AT*)a.q;
@@ -455,11 +602,11 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
     AT* o = (AT*)a.o;
     float scale = a.scale;
     void* args[] = {&T, &H, &q, &k, &v, &alpha, &beta, &state, &o, &scale};
-    return hipLaunchKernel((const void*)gdn_decode_kernel<G, AT>,
+    return hipLaunchKernel((const void*)gdn_decode_kernel<G, MULTI, AT>,
                            dim3((unsigned)(a.B * a.H * G::SPLIT)), dim3(G::NT), args, 0, s);
 }
 
-template <class G>
+template <class G, bool MULTI>
 hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
     int T = a.T, H = a.H;
     const uint16_t* qkv = (const uint16_t*)a.qkv;
@@ -472,40 +619,46 @@ hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
     uint16_t* o = (uint16_t*)a.o;
     float scale = a.scale, eps = a.l2_eps;
     void* args[] = {&T, &H, &qkv, &cs, &w, &cb, &al, &bl, &state, &o, &scale, &eps};
-    return hipLaunchKernel((const void*)gdn_conv_gate_decode_kernel<G>,
+    return hipLaunchKernel((const void*)gdn_conv_gate_decode_kernel<G, MULTI>,
                            dim3((unsigned)(a.B * a.H)), dim3(G::NT), args, 0, s);
 }
 
-// Launch geometry, chosen by sweeping every variant below on MI355X at B=256, H=48, D=128
-// (all variants produce bit-identical results; only the schedule differs):
+constexpr int min_int(int a, int b) { return a < b ? a : b; }
+constexpr int max_int(int a, int b) { return a > b ? a : b; }
+
+// Launch geometry, chosen by sweeping variants on MI355X at B=256, H=48, D=128 (variants with
+// the same lanes per row reproduce each other bit for bit; only the schedule differs):
 //  * one token, fp32 state: one wave per workgroup, 8 rows (4 KiB) per wave, nontemporal
-//    state loads and stores -- 78% of HBM peak; larger workgroups synchronise their waves'
+//    state loads and stores -- 79% of HBM peak; larger workgroups synchronise their waves'
 //    load/store phases and lose 5-15%;
 //  * one token, bf16 state: all rows of a head in one workgroup, 8 rows per wave;
-//  * several tokens: the per-token arithmetic matters (it is repeated T times on registers),
-//    so fewer, larger workgroups amortise the staging: fp32 4 waves x 8 rows with 4
-//    workgroups per head in XCD-contiguous order, bf16 4 waves x 32 rows.
-template <int D> constexpr int waves_for() { return D >= 32 ? D / 32 : 1; }
-constexpr int min_int(int a, int b) { return a < b ? a : b; }
-
+//  * several tokens (and the fused path): the per-token arithmetic is repeated on registers,
+//    so occupancy and instruction count decide: 16 rows per wave, one workgroup per head,
+//    8 lanes per row where it saves reduction steps (bf16 state, fused prologue).
 template <int D, typename ST> struct DecodeOneToken;
-template <int D> struct DecodeOneToken<D, float> { using G = Geo<D, float, 1, D / 8, 1, true, true>; };
-template <int D> struct DecodeOneToken<D, uint16_t> { using G = Geo<D, uint16_t, D / 8, 1, 1, true, true>; };
+template <int D> struct DecodeOneToken<D, float> {
+    using G = Geo<D, float, 1, D / 8, 1, true, true>;
+};
+template <int D> struct DecodeOneToken<D, uint16_t> {
+    using G = Geo<D, uint16_t, D / 8, 1, 1, true, true>;
+};
 
 template <int D, typename ST> struct DecodeTokens;
 template <int D> struct DecodeTokens<D, float> {
-    static constexpr int W = min_int(4, D / 8);
-    using G = Geo<D, float, W, D / (8 * W), 8, true, true, true>;
+    using G = Geo<D, float, max_int(1, D / 16), 1, 8, true, true, 0, 16>;
 };
-template <int D> struct DecodeTokens<D, uint16_t> { using G = Geo<D, uint16_t, waves_for<D>(), 1, 8, false, false>; };
+template <int D> struct DecodeTokens<D, uint16_t> {
+    using G = Geo<D, uint16_t, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
+};
 
-template <int D, typename ST>
-using FusedGeo = Geo<D, ST, waves_for<D>(), 1, 8, false, false>;
+template <int D, typename ST> struct FusedTokens {
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
+};
 
 template <int D, typename ST, typename AT>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-    if (a.T == 1) return launch_decode_g<typename DecodeOneToken<D, ST>::G, AT>(a, s);
-    return launch_decode_g<typename DecodeTokens<D, ST>::G, AT>(a, s);
+    if (a.T == 1) return launch_decode_g<typename DecodeOneToken<D, ST>::G, false, AT>(a, s);
+    return launch_decode_g<typename DecodeTokens<D, ST>::G, true, AT>(a, s);
 }
 
 template <int D>
@@ -517,10 +670,16 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     return launch_decode_t<D, uint16_t, uint16_t>(a, s);
 }
 
+template <int D, typename ST>
+hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
+    if (a.T == 1) return launch_fused_g<typename FusedTokens<D, ST>::G, false>(a, s);
+    return launch_fused_g<typename FusedTokens<D, ST>::G, true>(a, s);
+}
+
 template <int D>
 hipError_t launch_fused_d(const FusedArgs& a, hipStream_t s) {
-    if (a.state_dtype == DType::F32) return launch_fused_g<FusedGeo<D, float>>(a, s);
-    return launch_fused_g<FusedGeo<D, uint16_t>>(a, s);
+    if (a.state_dtype == DType::F32) return launch_fused_t<D, float>(a, s);
+    return launch_fused_t<D, uint16_t>(a, s);
 }
 
 }  // namespace

@@ -31,6 +31,7 @@ WORKLOADS = {
     "decode_b1_h48_d128_t1": dict(B=1, H=48, D=128, T=1, act="bf16", state_init="normal"),
     "decode_b64_h48_d128_t1": dict(B=64, H=48, D=128, T=1, act="bf16", state_init="normal"),
     "decode_b256_h48_d128_t1": dict(B=256, H=48, D=128, T=1, act="bf16", state_init="normal"),
+    "decode_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, act="bf16", state_init="normal"),
     "fused_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, fused=True),
 }
 

@@ -143,9 +143,11 @@ def test_bitwise_deterministic():
 
 
 def test_multi_token_call_equals_single_token_calls():
-    # fp32 state is stored and reloaded exactly, so splitting a call changes no bit.
+    # A T-token call keeps the state in registers as S / c (c the running product of alpha);
+    # one-token calls step S directly. Both are the same recurrence up to fp32 rounding, so the
+    # results agree to the fp32 bar, and every split of the tokens resumes correctly.
     _announce("T=5 vs 5 x T=1 vs 3+2")
-    x = to_dev(synth.decode_inputs(4, 6, 128, 5, seed=9))
+    x = to_dev(synth.decode_inputs(4, 6, 128, 5, alpha_shift=-2.0, seed=9))
     S_all = x["state"].clone()
     o_all = gdn.decode_step(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S_all)
     S_one = x["state"].clone()
@@ -159,10 +161,32 @@ def test_multi_token_call_equals_single_token_calls():
     o_a = gdn.decode_step(*(x[n][:, :3].contiguous() for n in ("q", "k", "v", "alpha", "beta")), S_split)
     o_b = gdn.decode_step(*(x[n][:, 3:].contiguous() for n in ("q", "k", "v", "alpha", "beta")), S_split)
     torch.cuda.synchronize()
-    assert torch.equal(S_all, S_one) and torch.equal(S_all, S_split)
-    o_one = torch.cat(outs, dim=1)
-    assert torch.equal(o_all.view(torch.int16), o_one.view(torch.int16))
-    assert torch.equal(o_all.view(torch.int16), torch.cat([o_a, o_b], 1).view(torch.int16))
+    check_state(f64(S_one), f64(S_all), torch.float32)
+    check_state(f64(S_split), f64(S_all), torch.float32)
+    check_o(f64(torch.cat(outs, dim=1)), f64(o_all), torch.bfloat16)
+    check_o(f64(torch.cat([o_a, o_b], 1)), f64(o_all), torch.bfloat16)
+    S_ref, o_ref = oracle_decode(synth.decode_inputs(4, 6, 128, 5, alpha_shift=-2.0, seed=9))
+    check_state(f64(S_all), S_ref, torch.float32)
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_multi_token_scale_fold_paths(sdt):
+    # Decays that push the running scale out of [2^-64, 2^64] or to zero: alpha = 0 mid-call,
+    # alpha = 1e-30, and alpha = 1.7 for 100 tokens (growth past 2^64 after ~84 tokens).
+    _announce(f"scale fold-back paths state={sdt}")
+    B, H, D, T = 2, 3, 64, 100
+    x = synth.decode_inputs(B, H, D, T, state_dtype=sdt, seed=13)
+    a = x["alpha"]
+    a[0, :, 0] = 1.7
+    a[0, 5, 1] = 0.0
+    a[0, 50, 1] = 0.0
+    a[1, ::7, 2] = 1e-30
+    a[1, :, 0] = 1.0
+    x["beta"][1, :, 0] = 0.0
+    S, o = gpu_decode(x)
+    S_ref, o_ref = oracle_decode(x)
+    check_state(f64(S), S_ref, DT[sdt])
+    check_o(f64(o), o_ref, torch.bfloat16)
 
 
 def test_empty_calls_change_nothing():
@@ -223,3 +247,41 @@ def test_state_beyond_4_GiB_offsets():
                                      f64(sel(beta))[:, :, None], f64(S0_s)[:, None])
     check_state(f64(S1_s), S_ref[:, 0], torch.float32)
     check_o(f64(o.cpu()[torch.as_tensor(b), :, torch.as_tensor(h)]), o_ref[:, :, 0], torch.bfloat16)
+
+
+def test_bf16_state_store_rounds_to_nearest_even():
+    # alpha = 0, beta = 1, zero state, k = e_j, fp32 activations: the new state's column j is v
+    # exactly in fp32, so the stored bf16 column must equal torch's CPU round-to-nearest-even
+    # of v, bit for bit (ties both ways, near-ties, overflow to infinity, denormals, NaN).
+    _announce("bf16 state rounding")
+    B, H, D = 4, 64, 128
+    rng = np.random.default_rng(14)
+    n = B * H * D
+    bits = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    finite = (bits & 0x7F800000) != 0x7F800000
+    bits = np.where(finite, bits, bits & 0x3FFFFFFF)          # random finite patterns
+    special = np.array([0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0xBF808000,
+                        0xBF818000, 0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x00008000,
+                        0x00018000, 0x00000001, 0x007FFFFF, 0x7F800000, 0xFF800000,
+                        0x7FC00000, 0x7F800001, 0x3F800000, 0x00000000], dtype=np.uint32)
+    bits[: special.size] = special
+    ties = rng.integers(0, 2 ** 16, 4096, dtype=np.uint64).astype(np.uint32)
+    bits[1000:1000 + 4096] = ((ties & 0x7EFF) << 16) | 0x8000    # exact ties, both parities
+    v = torch.from_numpy(bits.view(np.float32).copy()).reshape(B, 1, H, D)
+    k = torch.zeros(B, 1, H, D)
+    js = (torch.arange(B * H) % D).reshape(B, H)
+    for b in range(B):
+        for h in range(H):
+            k[b, 0, h, js[b, h]] = 1.0
+    q = k.clone()
+    alpha = torch.zeros(B, 1, H)
+    beta = torch.ones(B, 1, H)
+    state = torch.zeros(B, H, D, D, dtype=torch.bfloat16)
+    x = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, state=state)
+    S, _ = gpu_decode(x)
+    S = S.cpu()
+    got = torch.stack([S[b, h, :, js[b, h]] for b in range(B) for h in range(H)]).reshape(-1)
+    want = v.reshape(B * H, D).to(torch.bfloat16).reshape(-1)
+    gn, wn = torch.isnan(got.float()), torch.isnan(want.float())
+    assert torch.equal(gn, wn)
+    assert torch.equal(got[~gn].view(torch.int16), want[~wn].view(torch.int16))
