@@ -56,10 +56,12 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16", "f16"])
     ap.add_argument("--layers", type=int, default=0, help="layer buffers rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
+    ap.add_argument("--graph-groups", type=int, default=7, help="graph-replay groups (0 = skip)")
+    ap.add_argument("--graph-replays", type=int, default=400, help="launches per graph replay")
     return ap.parse_args(argv)
 
 
@@ -157,7 +159,44 @@ def time_gpu(args, spec, workload):
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
-    return ms_total / args.steps, L
+
+    extra = {}
+    if args.graph_groups > 0:
+        # The same launches replayed from a HIP graph: median over groups of the mean per
+        # launch, each group one replay of `graph_replays` captured launches.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.graph_replays):
+                step(layers[i % L])
+        g.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(args.graph_groups):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(torch.cuda.current_stream(dev))
+            g.replay()
+            e1.record(torch.cuda.current_stream(dev))
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / args.graph_replays)
+        per.sort()
+        extra["graph_median_us"] = per[len(per) // 2] * 1e3
+        extra["graph_protocol"] = f"median of {args.graph_groups} graph replays x {args.graph_replays} launches"
+        del g
+    # Plain device copy of the same number of state bytes: the read+write ceiling of this machine.
+    src = layers[0]["state"]
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(50):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    nb = 2 * src.numel() * src.element_size()
+    extra["copy_gbps_same_bytes"] = nb / (e0.elapsed_time(e1) / 50 * 1e-3) / 1e9
+    return ms_total / args.steps, L, extra
 
 
 def time_copy(args, mb: int):
@@ -243,7 +282,7 @@ def main(argv=None):
 
     from gated_deltanet_recurrent_02_amd import synth
     spec = dict(synth.WORKLOADS[args.workload])
-    ms, L = time_gpu(args, spec, args.workload)
+    ms, L, extra = time_gpu(args, spec, args.workload)
     us = ms * 1e3
     nbytes = algorithmic_bytes(spec, args.state_dtype)
     gbps = nbytes / (ms * 1e-3) / 1e9
@@ -267,6 +306,8 @@ def main(argv=None):
                      "kernel_source_sha256_16": kernel_source_hash()},
         "gflops": flops(spec) / (ms * 1e-3) / 1e9,
     }
+    line.update(extra)
+    line["frac_of_copy_bw"] = gbps / extra["copy_gbps_same_bytes"]
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(spec, args.workload, args.state_dtype, args.cpu_seconds)

@@ -15,9 +15,9 @@ import torch
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_OUT_OF_MEMORY, GDN_ERR_HIP = range(5)
-GDN_F32, GDN_BF16 = 0, 1
-_DTYPE_CODE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
-_CODE_DTYPE = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16}
+GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: GDN_F16}
+_CODE_DTYPE = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16, GDN_F16: torch.float16}
 
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_state_alloc", "gdn_state_free", "gdn_decode_step", "gdn_conv_gate_decode",
@@ -93,14 +93,15 @@ def _need(t: torch.Tensor, name: str, shape: tuple, dtypes: tuple) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-_ACT = (torch.float32, torch.bfloat16)
+_ACT = (torch.float32, torch.bfloat16, torch.float16)
 
 
 def decode_step(q, k, v, alpha, beta, state, o=None, scale: float = 1.0):
     """gdn_decode_step on torch tensors; updates `state` in place and returns o.
 
-    q, k [B,T,H,dk] and v [B,T,H,dv] share one dtype (fp32 or bf16); alpha, beta fp32 [B,T,H];
-    state fp32 or bf16 [B,H,dv,dk]; o (optional) [B,T,H,dv] in the activation dtype."""
+    q, k [B,T,H,dk] and v [B,T,H,dv] share one dtype (fp32, bf16 or fp16); alpha, beta fp32
+    [B,T,H]; state fp32, bf16 or fp16 [B,H,dv,dk]; o (optional) [B,T,H,dv] in the activation
+    dtype."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     _need(q, "q", (B, T, H, dk), _ACT)
@@ -125,7 +126,7 @@ def conv_gate_decode(qkv, conv_state, conv_w, conv_b, a_logit, b_logit, state, o
 
     qkv bf16 [B,T,C] with C = 3*H*D (blocks q | k | v); conv_state bf16 [B,C,3];
     conv_w fp32 [C,4]; conv_b fp32 [C] or None; a_logit, b_logit fp32 [B,T,H];
-    state fp32 or bf16 [B,H,D,D]."""
+    state fp32, bf16 or fp16 [B,H,D,D]."""
     B, T, C = qkv.shape
     H = a_logit.shape[-1]
     D = state.shape[-1]
@@ -166,13 +167,13 @@ class StateBuffer:
 
     @property
     def __cuda_array_interface__(self):
-        typestr = "<f4" if self.dtype == torch.float32 else "<V2"
+        typestr = {torch.float32: "<f4", torch.float16: "<f2"}.get(self.dtype, "<V2")
         return {"shape": self.shape, "typestr": typestr, "data": (self.ptr, False),
                 "version": 2, "strides": None}
 
     def tensor(self) -> torch.Tensor:
         """A torch view of the buffer (bf16 buffers are reinterpreted from 2-byte words)."""
-        if self.dtype == torch.float32:
+        if self.dtype in (torch.float32, torch.float16):
             return torch.as_tensor(self, device="cuda")
         iface = {"shape": self.shape, "typestr": "<i2", "data": (self.ptr, False),
                  "version": 2, "strides": None}

@@ -27,8 +27,11 @@ gdn_status fail_hip(const char* what, hipError_t e) {
 }
 
 bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
-bool valid_dtype(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16; }
+bool valid_dtype(gdn_dtype t) { return t == GDN_F32 || t == GDN_BF16 || t == GDN_F16; }
 size_t dtype_bytes(gdn_dtype t) { return t == GDN_F32 ? 4 : 2; }
+gdn::DType to_dtype(gdn_dtype t) {
+    return t == GDN_F32 ? gdn::DType::F32 : (t == GDN_BF16 ? gdn::DType::BF16 : gdn::DType::F16);
+}
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // a * b with overflow detection on size_t.
@@ -169,10 +172,10 @@ gdn_status gdn_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t 
     gdn::DecodeArgs a;
     a.B = B; a.T = T; a.H = H; a.D = dk;
     a.q = q; a.k = k; a.v = v;
-    a.act = act_dtype == GDN_F32 ? gdn::DType::F32 : gdn::DType::BF16;
+    a.act = to_dtype(act_dtype);
     a.alpha = alpha; a.beta = beta;
     a.state = state;
-    a.state_dtype = state_dtype == GDN_F32 ? gdn::DType::F32 : gdn::DType::BF16;
+    a.state_dtype = to_dtype(state_dtype);
     a.o = o; a.scale = scale;
     hipError_t e = gdn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip("gdn_decode_step: kernel launch", e);
@@ -220,7 +223,7 @@ gdn_status gdn_conv_gate_decode(int64_t B, int32_t T, int32_t H, int32_t dk, int
     a.qkv = qkv; a.conv_state = conv_state; a.conv_w = conv_w; a.conv_b = conv_b;
     a.a_logit = a_logit; a.b_logit = b_logit;
     a.state = state;
-    a.state_dtype = state_dtype == GDN_F32 ? gdn::DType::F32 : gdn::DType::BF16;
+    a.state_dtype = to_dtype(state_dtype);
     a.o = o; a.scale = scale; a.l2_eps = l2_eps;
     hipError_t e = gdn::launch_conv_gate_decode(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip("gdn_conv_gate_decode: kernel launch", e);

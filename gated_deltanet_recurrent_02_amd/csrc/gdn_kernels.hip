@@ -7,7 +7,7 @@
 // which is S_t = alpha S_{t-1}(I - beta k k^T) + beta v k^T, o_t = S_t q_t regrouped so that the
 // state is read once and written once.
 //
-// The work is a stream: per token a head moves its 64 KiB fp32 state (or 32 KiB bf16) through
+// The work is a stream: per token a head moves its 64 KiB fp32 state (32 KiB bf16/fp16) through
 // ~6 flop per element, far below the chip's flop:byte ridge, so no matrix cores are used and
 // the layout exists to keep every HBM access a full, coalesced line:
 //   * state [B][H][D][D], row i (value dim) contiguous over the key dim;
@@ -61,6 +61,41 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) { return f32x2_to_bf16x2(f, 0.0f) & 0xffffu; }
 
+// fp16 (IEEE binary16) storage: _Float16. Stores round to nearest even (v_cvt_pk_f16_f32; not
+// the round-toward-zero pkrtz form); loads widen exactly.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+__device__ __forceinline__ f32x2_t f16x2_to_f32x2(uint32_t bits) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2_t, bits), f32x2_t);
+}
+
+// Storage element types: float (fp32), uint16_t (bf16 bits), _Float16 (fp16).
+template <typename T> struct is_f16 { static constexpr bool value = false; };
+template <> struct is_f16<_Float16> { static constexpr bool value = true; };
+
+// Two floats packed into one 32-bit word of the 2-byte storage type ST.
+template <typename ST>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if constexpr (is_f16<ST>::value) return f32x2_to_f16x2(lo, hi);
+    else return f32x2_to_bf16x2(lo, hi);
+}
+
+// Element e (0 = low half, 1 = high half) of a 32-bit word of the 2-byte storage type ST.
+template <typename ST>
+__device__ __forceinline__ float unpack(uint32_t word, int e) {
+    if constexpr (is_f16<ST>::value) {
+        const f32x2_t f = f16x2_to_f32x2(word);
+        return e ? f.y : f.x;
+    } else {
+        return e ? __uint_as_float(word & 0xffff0000u) : bf16_to_f32(word & 0xffffu);
+    }
+}
+
 // A value every lane of the wave holds identically, moved to a scalar register.
 __device__ __forceinline__ float uniform(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
@@ -68,10 +103,14 @@ __device__ __forceinline__ float uniform(float x) {
 
 __device__ __forceinline__ float act_to_f32(float x) { return x; }
 __device__ __forceinline__ float act_to_f32(uint16_t x) { return bf16_to_f32(x); }
+__device__ __forceinline__ float act_to_f32(_Float16 x) { return (float)x; }
 template <typename AT> __device__ __forceinline__ AT act_from_f32(float x);
 template <> __device__ __forceinline__ float act_from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ uint16_t act_from_f32<uint16_t>(float x) {
     return (uint16_t)f32_to_bf16(x);
+}
+template <> __device__ __forceinline__ _Float16 act_from_f32<_Float16>(float x) {
+    return __builtin_bit_cast(_Float16, (uint16_t)(f32x2_to_f16x2(x, 0.0f) & 0xffffu));
 }
 
 // ------------------------------------------------------------------------ DPP reductions
@@ -232,8 +271,7 @@ __device__ __forceinline__ void load_state(const typename G::ST* __restrict__ Sg
                 if constexpr (sizeof(ST) == 4) {
                     x = __uint_as_float(w.w[e]);
                 } else {
-                    const uint32_t word = w.w[e >> 1];
-                    x = (e & 1) ? __uint_as_float(word & 0xffff0000u) : bf16_to_f32(word & 0xffffu);
+                    x = unpack<ST>(w.w[e >> 1], e & 1);
                 }
                 S[p][c * G::VW + e] = x;
             }
@@ -258,7 +296,7 @@ __device__ __forceinline__ void store_state(typename G::ST* __restrict__ Sg, int
 #pragma unroll
                 for (int e = 0; e < G::VW; e += 2) {
                     const float hi = (e + 1 < G::VW) ? S[p][c * G::VW + e + 1] : 0.0f;
-                    w.w[e >> 1] = f32x2_to_bf16x2(S[p][c * G::VW + e], hi);
+                    w.w[e >> 1] = pack2<ST>(S[p][c * G::VW + e], hi);
                 }
             }
             gstore<G::VB, G::NTS>(rowp + c * G::LPR * G::VW + l * G::VW, w);
@@ -458,12 +496,19 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     for (int t0 = 0; t0 < T; t0 += G::TCH) {
         const int nt = min(G::TCH, T - t0);
         if (t0 > 0) __syncthreads();  // the previous round's readers are done with L
-        for (int i = tid; i < nt * 3 * D; i += G::NT) {
-            const int tt = i / (3 * D), r = i - tt * 3 * D, which = r / D, j = r - which * D;
+        // q and k in full; v only for this workgroup's rows.
+        constexpr int NV = 2 * D + G::RPG;
+        for (int i = tid; i < nt * NV; i += G::NT) {
+            const int tt = i / NV, r = i - tt * NV;
             const size_t tok = ((size_t)b * T + t0 + tt) * H + h;
-            const AT* src = which == 0 ? q : (which == 1 ? k : v);
-            const float x = act_to_f32(src[tok * D + j]);
-            if (which == 0) L.q[tt][j] = x; else if (which == 1) L.k[tt][j] = x; else L.v[tt][j] = x;
+            if (r < D) {
+                L.q[tt][r] = act_to_f32(q[tok * D + r]);
+            } else if (r < 2 * D) {
+                L.k[tt][r - D] = act_to_f32(k[tok * D + r - D]);
+            } else {
+                const int j = part * G::RPG + (r - 2 * D);
+                L.v[tt][j] = act_to_f32(v[tok * D + j]);
+            }
         }
         if (tid < nt) {
             const size_t tok = ((size_t)b * T + t0 + tid) * H + h;
@@ -623,7 +668,6 @@ hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
                            dim3((unsigned)(a.B * a.H)), dim3(G::NT), args, 0, s);
 }
 
-constexpr int min_int(int a, int b) { return a < b ? a : b; }
 constexpr int max_int(int a, int b) { return a > b ? a : b; }
 
 // Launch geometry, chosen by sweeping variants on MI355X at B=256, H=48, D=128 (variants with
@@ -635,20 +679,18 @@ constexpr int max_int(int a, int b) { return a > b ? a : b; }
 //  * several tokens (and the fused path): the per-token arithmetic is repeated on registers,
 //    so occupancy and instruction count decide: 16 rows per wave, one workgroup per head,
 //    8 lanes per row where it saves reduction steps (bf16 state, fused prologue).
-template <int D, typename ST> struct DecodeOneToken;
+template <int D, typename ST> struct DecodeOneToken {  // 2-byte states
+    using G = Geo<D, ST, D / 8, 1, 1, true, true>;
+};
 template <int D> struct DecodeOneToken<D, float> {
     using G = Geo<D, float, 1, D / 8, 1, true, true>;
 };
-template <int D> struct DecodeOneToken<D, uint16_t> {
-    using G = Geo<D, uint16_t, D / 8, 1, 1, true, true>;
-};
 
-template <int D, typename ST> struct DecodeTokens;
+template <int D, typename ST> struct DecodeTokens {  // 2-byte states
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
+};
 template <int D> struct DecodeTokens<D, float> {
     using G = Geo<D, float, max_int(1, D / 16), 1, 8, true, true, 0, 16>;
-};
-template <int D> struct DecodeTokens<D, uint16_t> {
-    using G = Geo<D, uint16_t, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
 };
 
 template <int D, typename ST> struct FusedTokens {
@@ -661,13 +703,22 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     return launch_decode_g<typename DecodeTokens<D, ST>::G, true, AT>(a, s);
 }
 
+template <int D, typename ST>
+hipError_t launch_decode_s(const DecodeArgs& a, hipStream_t s) {
+    switch (a.act) {
+        case DType::F32: return launch_decode_t<D, ST, float>(a, s);
+        case DType::BF16: return launch_decode_t<D, ST, uint16_t>(a, s);
+        default: return launch_decode_t<D, ST, _Float16>(a, s);
+    }
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
-    const bool sf = a.state_dtype == DType::F32, af = a.act == DType::F32;
-    if (sf && af) return launch_decode_t<D, float, float>(a, s);
-    if (sf) return launch_decode_t<D, float, uint16_t>(a, s);
-    if (af) return launch_decode_t<D, uint16_t, float>(a, s);
-    return launch_decode_t<D, uint16_t, uint16_t>(a, s);
+    switch (a.state_dtype) {
+        case DType::F32: return launch_decode_s<D, float>(a, s);
+        case DType::BF16: return launch_decode_s<D, uint16_t>(a, s);
+        default: return launch_decode_s<D, _Float16>(a, s);
+    }
 }
 
 template <int D, typename ST>
@@ -678,8 +729,11 @@ hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_fused_d(const FusedArgs& a, hipStream_t s) {
-    if (a.state_dtype == DType::F32) return launch_fused_t<D, float>(a, s);
-    return launch_fused_t<D, uint16_t>(a, s);
+    switch (a.state_dtype) {
+        case DType::F32: return launch_fused_t<D, float>(a, s);
+        case DType::BF16: return launch_fused_t<D, uint16_t>(a, s);
+        default: return launch_fused_t<D, _Float16>(a, s);
+    }
 }
 
 }  // namespace

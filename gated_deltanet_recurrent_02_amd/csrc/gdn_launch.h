@@ -8,7 +8,7 @@
 
 namespace gdn {
 
-enum class DType : int { F32 = 0, BF16 = 1 };
+enum class DType : int { F32 = 0, BF16 = 1, F16 = 2 };
 
 struct DecodeArgs {
     int64_t B;

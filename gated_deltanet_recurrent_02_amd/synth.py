@@ -16,14 +16,15 @@ Recipes (no trained weights or live activations exist for this path, so these st
       qkv ~ N(0, 1) bf16 [B,T,C], conv_state ~ N(0, 1) bf16 [B,C,3], conv_w ~ N(0, 0.5) fp32 [C,4],
       a_logit, b_logit ~ N(0, 1) fp32 [B,T,H], state ~ N(0, 0.02)
     draw order: qkv, conv_state, conv_w, a_logit, b_logit, state.
-Every narrower type is the round-to-nearest-even image of the fp32/fp64 draw (torch's cast).
+Every narrower type (bf16, fp16) is the round-to-nearest-even image of the fp32/fp64 draw
+(torch's cast).
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 # Named workloads: batch B, heads H, head dim D (dk = dv), tokens per call T.
 WORKLOADS = {

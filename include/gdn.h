@@ -52,7 +52,9 @@ typedef enum {
 
 typedef enum {
     GDN_F32 = 0,  /* IEEE binary32 */
-    GDN_BF16 = 1  /* bfloat16; every bf16 store rounds to nearest even */
+    GDN_BF16 = 1, /* bfloat16; every bf16 store rounds to nearest even */
+    GDN_F16 = 2   /* IEEE binary16; every fp16 store rounds to nearest even (the reduced-
+                     precision mode of "GDN tuning limits on Kunlun XPU", section 三.2) */
 } gdn_dtype;
 
 /*
@@ -87,8 +89,10 @@ gdn_status gdn_state_free(void* state);
  *                                    argument (checked by address range)
  *   scale  multiplies q in the readout (1.0f = the plain definition)
  *
- * Arithmetic is fp32 (bf16 inputs widen exactly); a bf16 state is widened on load, kept in fp32
- * across the T tokens of the call and rounded once when stored.
+ * Arithmetic is fp32 (bf16 and fp16 inputs widen exactly); a 16-bit state is widened on load,
+ * kept in fp32 across the T tokens of the call and rounded once when stored. An fp16 state or
+ * output saturates to infinity beyond 65504; keeping values in range is the caller's choice
+ * of that dtype.
  * Errors: GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP (see conventions).
  */
 gdn_status gdn_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,

@@ -16,7 +16,7 @@ from parity import (check_o, check_state, f64, gpu_decode, oracle_decode, sample
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def _announce(msg):
@@ -33,8 +33,8 @@ def test_tiny_workload_full_compare():
 
 
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
-@pytest.mark.parametrize("act", ["f32", "bf16"])
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("B,H,T", [(3, 5, 1), (2, 3, 11)])
 def test_small_shapes_full_compare(D, act, sdt, B, H, T):
     _announce(f"decode B={B} H={H} D={D} T={T} act={act} state={sdt}")
@@ -48,7 +48,7 @@ def test_small_shapes_full_compare(D, act, sdt, B, H, T):
 @pytest.mark.parametrize("name,alpha_shift", [
     ("decode_b1_h48_d128_t1", 2.0), ("decode_b1_h48_d128_t1", -2.0),
     ("decode_b64_h48_d128_t1", 2.0), ("decode_b256_h48_d128_t1", 2.0)])
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
 def test_full_size_workloads_sampled(name, alpha_shift, sdt):
     _announce(f"{name} alpha_shift={alpha_shift} state={sdt}")
     x = synth.workload_inputs(name, alpha_shift=alpha_shift, state_dtype=sdt)
@@ -60,9 +60,9 @@ def test_full_size_workloads_sampled(name, alpha_shift, sdt):
     check_o(f64(o[b, :, h]), o_ref, torch.bfloat16)
 
 
-def test_t4_on_full_heads_fp32_and_bf16():
+def test_t4_on_full_heads_all_state_dtypes():
     # Multi-token decode at the bottleneck head count, B=8: all heads compared.
-    for sdt in ("f32", "bf16"):
+    for sdt in ("f32", "bf16", "f16"):
         _announce(f"decode B=8 H=48 D=128 T=4 state={sdt}")
         x = synth.decode_inputs(8, 48, 128, 4, state_dtype=sdt, alpha_shift=-2.0, seed=3)
         S, o = gpu_decode(x)
@@ -74,7 +74,7 @@ def test_t4_on_full_heads_fp32_and_bf16():
 # ------------------------------------------------------------------ invariants
 
 
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
 def test_identity_gate_leaves_state_bit_identical(sdt):
     _announce(f"identity gate state={sdt}")
     x = synth.decode_inputs(4, 6, 128, 3, state_dtype=sdt, seed=4)
@@ -82,8 +82,8 @@ def test_identity_gate_leaves_state_bit_identical(sdt):
     x["beta"].fill_(0.0)
     S0 = x["state"].clone()
     S, o = gpu_decode(x)
-    assert torch.equal(S.cpu().view(torch.int16 if sdt == "bf16" else torch.int32),
-                       S0.view(torch.int16 if sdt == "bf16" else torch.int32))
+    assert torch.equal(S.cpu().view(torch.int16 if sdt != "f32" else torch.int32),
+                       S0.view(torch.int16 if sdt != "f32" else torch.int32))
     _, o_ref = oracle_decode(x)
     check_o(f64(o), o_ref, torch.bfloat16)
 
@@ -169,15 +169,17 @@ def test_multi_token_call_equals_single_token_calls():
     check_state(f64(S_all), S_ref, torch.float32)
 
 
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
 def test_multi_token_scale_fold_paths(sdt):
     # Decays that push the running scale out of [2^-64, 2^64] or to zero: alpha = 0 mid-call,
-    # alpha = 1e-30, and alpha = 1.7 for 100 tokens (growth past 2^64 after ~84 tokens).
+    # alpha = 1e-30, and alpha = 1.7 for 100 tokens (growth past 2^64 after ~84 tokens; fp32
+    # and bf16 states only, since fp16 cannot hold the grown state).
     _announce(f"scale fold-back paths state={sdt}")
     B, H, D, T = 2, 3, 64, 100
     x = synth.decode_inputs(B, H, D, T, state_dtype=sdt, seed=13)
     a = x["alpha"]
-    a[0, :, 0] = 1.7
+    # the true state grows as 1.7^100 (~1e23): representable in fp32/bf16, not in fp16
+    a[0, :, 0] = 1.7 if sdt != "f16" else 1.0
     a[0, 5, 1] = 0.0
     a[0, 50, 1] = 0.0
     a[1, ::7, 2] = 1e-30
@@ -249,11 +251,12 @@ def test_state_beyond_4_GiB_offsets():
     check_o(f64(o.cpu()[torch.as_tensor(b), :, torch.as_tensor(h)]), o_ref[:, :, 0], torch.bfloat16)
 
 
-def test_bf16_state_store_rounds_to_nearest_even():
+@pytest.mark.parametrize("sdt", ["bf16", "f16"])
+def test_16bit_state_store_rounds_to_nearest_even(sdt):
     # alpha = 0, beta = 1, zero state, k = e_j, fp32 activations: the new state's column j is v
-    # exactly in fp32, so the stored bf16 column must equal torch's CPU round-to-nearest-even
+    # exactly in fp32, so the stored 16-bit column must equal torch's CPU round-to-nearest-even
     # of v, bit for bit (ties both ways, near-ties, overflow to infinity, denormals, NaN).
-    _announce("bf16 state rounding")
+    _announce(f"{sdt} state rounding")
     B, H, D = 4, 64, 128
     rng = np.random.default_rng(14)
     n = B * H * D
@@ -266,7 +269,14 @@ def test_bf16_state_store_rounds_to_nearest_even():
                         0x7FC00000, 0x7F800001, 0x3F800000, 0x00000000], dtype=np.uint32)
     bits[: special.size] = special
     ties = rng.integers(0, 2 ** 16, 4096, dtype=np.uint64).astype(np.uint32)
-    bits[1000:1000 + 4096] = ((ties & 0x7EFF) << 16) | 0x8000    # exact ties, both parities
+    if sdt == "bf16":
+        bits[1000:1000 + 4096] = ((ties & 0x7EFF) << 16) | 0x8000    # exact ties, both parities
+    else:
+        # fp16 keeps 10 of fp32's 23 mantissa bits: a tie has the low 13 bits 0x1000; exponents
+        # around the fp16 range (normal, subnormal, overflow)
+        exps = rng.integers(96, 146, 4096, dtype=np.uint64).astype(np.uint32)
+        bits[1000:1000 + 4096] = (exps << 23) | ((ties & 0x3FF) << 13) | 0x1000
+        bits[1000:1000 + 4096] |= (ties & 0x8000) << 16
     v = torch.from_numpy(bits.view(np.float32).copy()).reshape(B, 1, H, D)
     k = torch.zeros(B, 1, H, D)
     js = (torch.arange(B * H) % D).reshape(B, H)
@@ -276,12 +286,12 @@ def test_bf16_state_store_rounds_to_nearest_even():
     q = k.clone()
     alpha = torch.zeros(B, 1, H)
     beta = torch.ones(B, 1, H)
-    state = torch.zeros(B, H, D, D, dtype=torch.bfloat16)
+    state = torch.zeros(B, H, D, D, dtype=DT[sdt])
     x = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, state=state)
     S, _ = gpu_decode(x)
     S = S.cpu()
     got = torch.stack([S[b, h, :, js[b, h]] for b in range(B) for h in range(H)]).reshape(-1)
-    want = v.reshape(B * H, D).to(torch.bfloat16).reshape(-1)
+    want = v.reshape(B * H, D).to(DT[sdt]).reshape(-1)
     gn, wn = torch.isnan(got.float()), torch.isnan(want.float())
     assert torch.equal(gn, wn)
     assert torch.equal(got[~gn].view(torch.int16), want[~wn].view(torch.int16))

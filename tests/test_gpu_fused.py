@@ -15,7 +15,7 @@ from parity import check_o, check_state, f64, to_dev
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def _announce(msg):
@@ -39,7 +39,7 @@ def oracle_fused(x, scale=1.0, l2_eps=1e-6):
 
 
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("B,H,T,bias", [(3, 5, 1, False), (2, 3, 4, True), (2, 2, 11, False)])
 def test_small_shapes_full_compare(D, sdt, B, H, T, bias):
     _announce(f"fused B={B} H={H} D={D} T={T} state={sdt} bias={bias}")
@@ -51,7 +51,7 @@ def test_small_shapes_full_compare(D, sdt, B, H, T, bias):
     check_o(f64(o), o_ref, torch.bfloat16)
 
 
-@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("sdt", ["f32", "bf16", "f16"])
 def test_full_size_fused_workload_sampled(sdt):
     _announce(f"fused_b256_h48_d128_t4 state={sdt}")
     x = synth.workload_inputs("fused_b256_h48_d128_t4", state_dtype=sdt)
