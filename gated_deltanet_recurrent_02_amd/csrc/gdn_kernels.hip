@@ -470,6 +470,76 @@ __device__ __forceinline__ void recur_tokens(float (&S)[G::P][G::E],
     }
 }
 
+// ------------------------------------------------------------------------ token staging
+
+// The per-token vectors a workgroup needs -- q and k in full, v for its own rows -- moved to
+// LDS in 16-byte chunks. fetch() issues the global loads into registers and commit() converts
+// and writes them, so the first round's loads can be issued before the state loads (the wait
+// for them then does not wait for the state) and each lane waits once, not once per element.
+template <class G, typename AT>
+struct TokenStage {
+    static constexpr int D = G::D;
+    static constexpr int CHK = 16 / (int)sizeof(AT);          // elements per 16-byte chunk
+    static constexpr int NQ = D / CHK, NV = G::RPG / CHK;     // chunks of q (= of k), of v
+    static constexpr int NCH = 2 * NQ + NV;                   // chunks per token
+    static constexpr int CPL = (G::TCH * NCH + G::NT - 1) / G::NT;  // chunks per lane, max
+    static_assert(D % CHK == 0 && G::RPG % CHK == 0, "rows must fill whole 16-byte chunks");
+    u32x4 raw[CPL];
+    float al = 0.f, be = 0.f;
+
+    __device__ __forceinline__ void fetch(const AT* __restrict__ q, const AT* __restrict__ k,
+                                          const AT* __restrict__ v, const float* __restrict__ alpha,
+                                          const float* __restrict__ beta, int64_t b, int T, int H,
+                                          int h, int part, int t0, int nt, int tid) {
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) {
+            const int c = tid + s * G::NT;
+            if (c < nt * NCH) {
+                const int tt = c / NCH, r = c - tt * NCH;
+                const size_t tok = ((size_t)b * T + t0 + tt) * H + h;
+                const AT* src = r < NQ ? q + tok * D + r * CHK
+                              : r < 2 * NQ ? k + tok * D + (r - NQ) * CHK
+                                           : v + tok * D + part * G::RPG + (r - 2 * NQ) * CHK;
+                raw[s] = *(const u32x4*)src;
+            }
+        }
+        if (tid < nt) {
+            const size_t tok = ((size_t)b * T + t0 + tid) * H + h;
+            al = alpha[tok];
+            be = beta[tok];
+        }
+    }
+
+    __device__ __forceinline__ void commit(TokLds<D, G::TCH>& L, int part, int nt, int tid,
+                                           float scale) const {
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) {
+            const int c = tid + s * G::NT;
+            if (c < nt * NCH) {
+                const int tt = c / NCH, r = c - tt * NCH;
+                float* dst = r < NQ ? &L.q[tt][r * CHK]
+                           : r < 2 * NQ ? &L.k[tt][(r - NQ) * CHK]
+                                        : &L.v[tt][part * G::RPG + (r - 2 * NQ) * CHK];
+                float f[CHK];
+                const uint32_t wv[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+#pragma unroll
+                for (int e = 0; e < CHK; ++e) {
+                    if constexpr (sizeof(AT) == 4) f[e] = __uint_as_float(wv[e]);
+                    else f[e] = unpack<AT>(wv[e >> 1], e & 1);
+                }
+#pragma unroll
+                for (int e = 0; e < CHK; e += 4) *(float4*)&dst[e] = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+            }
+        }
+        if (tid < nt) {
+            L.alpha[tid] = al;
+            L.beta[tid] = be;
+            L.qf[tid] = scale;
+            L.kf[tid] = 1.0f;
+        }
+    }
+};
+
 // ------------------------------------------------------------------------ decode kernel
 
 template <class G, bool MULTI, typename AT>
@@ -490,36 +560,49 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     const int rbase = part * G::RPG + wave * G::RPW;
 
     float S[G::P][G::E];
-    load_state<G>(Sg, rbase + g, l, S);
-
     float c = 1.0f;
-    for (int t0 = 0; t0 < T; t0 += G::TCH) {
-        const int nt = min(G::TCH, T - t0);
-        if (t0 > 0) __syncthreads();  // the previous round's readers are done with L
-        // q and k in full; v only for this workgroup's rows.
-        constexpr int NV = 2 * D + G::RPG;
-        for (int i = tid; i < nt * NV; i += G::NT) {
-            const int tt = i / NV, r = i - tt * NV;
-            const size_t tok = ((size_t)b * T + t0 + tt) * H + h;
-            if (r < D) {
-                L.q[tt][r] = act_to_f32(q[tok * D + r]);
-            } else if (r < 2 * D) {
-                L.k[tt][r - D] = act_to_f32(k[tok * D + r - D]);
-            } else {
-                const int j = part * G::RPG + (r - 2 * D);
-                L.v[tt][j] = act_to_f32(v[tok * D + j]);
+    if constexpr (G::TCH == 1) {
+        // One token per round (the one-token launch shape): stage q, k, v element by element
+        // after the state loads are issued. Measured on MI355X at B=256 H=48 D=128 T=1, this
+        // exact form (vector loads of alpha and beta by the lanes below nt) beats a 16-byte
+        // fetch issued before or after the state loads, and a scalar-load variant, by 1-3%.
+        load_state<G>(Sg, rbase + g, l, S);
+        for (int t0 = 0; t0 < T; t0 += G::TCH) {
+            const int nt = min(G::TCH, T - t0);
+            if (t0 > 0) __syncthreads();  // the previous round's readers are done with L
+            for (int i = tid; i < nt * 3 * D; i += G::NT) {
+                const int tt = i / (3 * D), r = i - tt * 3 * D, which = r / D, j = r - which * D;
+                const size_t tok = ((size_t)b * T + t0 + tt) * H + h;
+                const AT* src = which == 0 ? q : (which == 1 ? k : v);
+                const float x = act_to_f32(src[tok * D + j]);
+                if (which == 0) L.q[tt][j] = x; else if (which == 1) L.k[tt][j] = x; else L.v[tt][j] = x;
             }
+            if (tid < nt) {
+                const size_t tok = ((size_t)b * T + t0 + tid) * H + h;
+                L.alpha[tid] = alpha[tok];
+                L.beta[tid] = beta[tok];
+                L.qf[tid] = scale;
+                L.kf[tid] = 1.0f;
+            }
+            __syncthreads();
+            recur_tokens<G, MULTI, AT>(S, L, nt, rbase, g, l,
+                                       o + (((size_t)b * T + t0) * H + h) * D, (size_t)H * D, c);
         }
-        if (tid < nt) {
-            const size_t tok = ((size_t)b * T + t0 + tid) * H + h;
-            L.alpha[tid] = alpha[tok];
-            L.beta[tid] = beta[tok];
-            L.qf[tid] = scale;
-            L.kf[tid] = 1.0f;
+    } else {
+        TokenStage<G, AT> st;
+        st.fetch(q, k, v, alpha, beta, b, T, H, h, part, 0, min(G::TCH, T), tid);
+        load_state<G>(Sg, rbase + g, l, S);
+        for (int t0 = 0; t0 < T; t0 += G::TCH) {
+            const int nt = min(G::TCH, T - t0);
+            if (t0 > 0) {
+                __syncthreads();  // the previous round's readers are done with L
+                st.fetch(q, k, v, alpha, beta, b, T, H, h, part, t0, nt, tid);
+            }
+            st.commit(L, part, nt, tid, scale);
+            __syncthreads();
+            recur_tokens<G, MULTI, AT>(S, L, nt, rbase, g, l,
+                                       o + (((size_t)b * T + t0) * H + h) * D, (size_t)H * D, c);
         }
-        __syncthreads();
-        recur_tokens<G, MULTI, AT>(S, L, nt, rbase, g, l, o + (((size_t)b * T + t0) * H + h) * D,
-                                   (size_t)H * D, c);
     }
     if (MULTI && c != 1.0f) scale_state<G>(S, c);
     store_state<G>(Sg, rbase + g, l, S);
