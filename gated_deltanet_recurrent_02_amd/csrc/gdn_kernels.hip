@@ -633,13 +633,28 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
     typename G::ST* Sg = state + (size_t)n * D * D;
     const int rbase = wave * G::RPW;
 
-    float S[G::P][G::E];
-    load_state<G>(Sg, rbase + g, l, S);
-
-    // Per owned channel: taps, bias, and the rolling window of raw inputs (bf16 bits).
+    // Per owned channel: taps, bias, the rolling window of raw inputs (bf16 bits), and the
+    // round's new raw inputs. The first round's loads are all issued before the state loads.
     float tap[CPT][4], bias[CPT];
-    uint32_t win[CPT][3];
+    uint32_t win[CPT][3], xr[CPT][G::TCH];
     size_t chan[CPT];
+    float av = 0.f, bv = 0.f;
+    const int nt0 = min(G::TCH, T);
+    auto fetch_round = [&](int t0, int nt) {
+#pragma unroll
+        for (int s = 0; s < CPT; ++s) {
+            if (tid + s * G::NT < CH) {
+#pragma unroll
+                for (int tt = 0; tt < G::TCH; ++tt)
+                    if (tt < nt) xr[s][tt] = qkv[((size_t)b * T + t0 + tt) * C + chan[s]];
+            }
+        }
+        if (tid < nt) {
+            const size_t tok = ((size_t)b * T + t0 + tid) * H + h;
+            av = a_logit[tok];
+            bv = b_logit[tok];
+        }
+    };
 #pragma unroll
     for (int s = 0; s < CPT; ++s) {
         const int ci = tid + s * G::NT;
@@ -654,11 +669,18 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
             win[s][0] = cs[0]; win[s][1] = cs[1]; win[s][2] = cs[2];
         }
     }
+    fetch_round(0, nt0);
+
+    float S[G::P][G::E];
+    load_state<G>(Sg, rbase + g, l, S);
 
     float c = 1.0f;
     for (int t0 = 0; t0 < T; t0 += G::TCH) {
         const int nt = min(G::TCH, T - t0);
-        if (t0 > 0) __syncthreads();
+        if (t0 > 0) {
+            __syncthreads();
+            fetch_round(t0, nt);
+        }
         // Conv (kernel 4, tap 3 on the current input) + SiLU, into LDS.
 #pragma unroll
         for (int s = 0; s < CPT; ++s) {
@@ -666,22 +688,23 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
             if (ci < CH) {
                 const int blk = ci / D, j = ci - blk * D;
                 float* dst = blk == 0 ? &L.q[0][j] : (blk == 1 ? &L.k[0][j] : &L.v[0][j]);
-                for (int tt = 0; tt < nt; ++tt) {
-                    const uint32_t x = qkv[((size_t)b * T + t0 + tt) * C + chan[s]];
-                    float y = tap[s][0] * bf16_to_f32(win[s][0]);
-                    y = fmaf(tap[s][1], bf16_to_f32(win[s][1]), y);
-                    y = fmaf(tap[s][2], bf16_to_f32(win[s][2]), y);
-                    y = fmaf(tap[s][3], bf16_to_f32(x), y);
-                    y += bias[s];
-                    win[s][0] = win[s][1]; win[s][1] = win[s][2]; win[s][2] = x;
-                    dst[tt * D] = y / (1.0f + expf(-y));
+#pragma unroll
+                for (int tt = 0; tt < G::TCH; ++tt) {
+                    if (tt < nt) {
+                        const uint32_t x = xr[s][tt];
+                        float y = tap[s][0] * bf16_to_f32(win[s][0]);
+                        y = fmaf(tap[s][1], bf16_to_f32(win[s][1]), y);
+                        y = fmaf(tap[s][2], bf16_to_f32(win[s][2]), y);
+                        y = fmaf(tap[s][3], bf16_to_f32(x), y);
+                        y += bias[s];
+                        win[s][0] = win[s][1]; win[s][1] = win[s][2]; win[s][2] = x;
+                        dst[tt * D] = y / (1.0f + expf(-y));
+                    }
                 }
             }
         }
         // Gates: beta = sigma(b), alpha = exp(-softplus(a)).
         if (tid < nt) {
-            const size_t tok = ((size_t)b * T + t0 + tid) * H + h;
-            const float av = a_logit[tok], bv = b_logit[tok];
             L.beta[tid] = 1.0f / (1.0f + expf(-bv));
             L.alpha[tid] = expf(-(fmaxf(av, 0.0f) + log1pf(expf(-fabsf(av)))));
         }
