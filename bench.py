@@ -73,6 +73,13 @@ def algorithmic_bytes(spec: dict, state_dtype: str) -> int:
     B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
     sb = 4 if state_dtype == "f32" else 2
     state = 2 * B * H * D * D * sb
+    if spec.get("verify"):
+        from gated_deltanet_recurrent_02_amd import synth
+        ab = 4 if spec["act"] == "f32" else 2
+        n_acc = int(synth.accepted_prefix(B, T).sum())  # committed tokens over the batch
+        new = B * T * H * (3 * D * ab + 8 + D * ab + D * 4)       # q k v, gates, o, dk_out
+        prev = n_acc * H * (D * ab + 4 + D * 4)                    # k, alpha, dk of the prefix
+        return state + new + prev + B * 4
     if spec.get("fused"):
         C = 3 * H * D
         return (state + B * T * C * 2          # qkv in
@@ -123,6 +130,7 @@ def time_gpu(args, spec, workload):
     torch.cuda.set_device(dev)
     fused = spec.get("fused", False)
     x = synth.workload_inputs(workload, state_dtype=args.state_dtype)
+    x_B, x_T = x["B"], x["T"]
     state_bytes = x["state"].numel() * x["state"].element_size()
     L = args.layers or max(1, math.ceil(2 * MALL_BYTES / state_bytes))
     L = min(L, 64)
@@ -140,7 +148,20 @@ def time_gpu(args, spec, workload):
         layers.append(g)
     del x
 
-    if fused:
+    if spec.get("verify"):
+        n_acc = synth.accepted_prefix(x_B, x_T).to(dev)
+        for g in layers:
+            g["dk"] = [torch.zeros(g["v"].shape, dtype=torch.float32, device=dev) for _ in range(2)]
+            g["i"] = 0
+
+        def step(g):
+            # each round commits the previous round's accepted prefix (same token tensors)
+            j = g["i"] & 1
+            gdn.decode_verify(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state"],
+                              prev=(n_acc, g["k"], g["alpha"], g["dk"][1 - j]), o=g["o"],
+                              dk_out=g["dk"][j])
+            g["i"] += 1
+    elif fused:
         def step(g):
             gdn.conv_gate_decode(g["qkv"], g["conv_state"], g["conv_w"], g["conv_b"], g["a_logit"],
                                  g["b_logit"], g["state"], o=g["o"])
@@ -295,7 +316,8 @@ def main(argv=None):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "H": H, "dk": D, "dv": D, "T": T,
                    "state_dtype": args.state_dtype, "act_dtype": act,
-                   "entry_point": "gdn_conv_gate_decode" if spec.get("fused") else "gdn_decode_step",
+                   "entry_point": ("gdn_conv_gate_decode" if spec.get("fused") else
+                                   "gdn_decode_verify" if spec.get("verify") else "gdn_decode_step"),
                    "layers_rotated": L},
         "achieved_gbps": gbps,
         "seq_tokens_per_s": B * T / (ms * 1e-3),

@@ -20,8 +20,8 @@ _DTYPE_CODE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16, torch.float16: 
 _CODE_DTYPE = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16, GDN_F16: torch.float16}
 
 # Every symbol include/gdn.h declares.
-EXPORTS = ("gdn_state_alloc", "gdn_state_free", "gdn_decode_step", "gdn_conv_gate_decode",
-           "gdn_status_string", "gdn_last_error")
+EXPORTS = ("gdn_state_alloc", "gdn_state_free", "gdn_decode_step", "gdn_decode_verify",
+           "gdn_conv_gate_decode", "gdn_status_string", "gdn_last_error")
 
 
 class GDNError(RuntimeError):
@@ -55,6 +55,9 @@ def _declare(L):
     L.gdn_state_free.restype = i
     L.gdn_decode_step.argtypes = [i64, i32, i32, i32, i32, P, P, P, i, P, P, P, i, P, f32, P]
     L.gdn_decode_step.restype = i
+    L.gdn_decode_verify.argtypes = [i64, i32, i32, i32, i32, P, P, P, i, P, P, P, i, i32, P, P, P, P,
+                                    P, P, f32, P]
+    L.gdn_decode_verify.restype = i
     L.gdn_conv_gate_decode.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i, P, f32, f32, P]
     L.gdn_conv_gate_decode.restype = i
     L.gdn_status_string.argtypes = [i]
@@ -117,6 +120,45 @@ def decode_step(q, k, v, alpha, beta, state, o=None, scale: float = 1.0):
                                 _ptr(alpha), _ptr(beta), _ptr(state), _DTYPE_CODE[state.dtype],
                                 _ptr(o), float(scale), _stream(q.device)))
     return o
+
+
+def decode_verify(q, k, v, alpha, beta, state, prev=None, o=None, dk_out=None,
+                  scale: float = 1.0):
+    """gdn_decode_verify on torch tensors: commit the previous call's accepted prefix into
+    `state`, then run the new tokens without storing the state after them.
+
+    q, k, v, alpha, beta as decode_step (T may be 0 to commit only; pass tensors with T = 0).
+    prev: None for the first call, else (n_prev int32 [B], k_prev [B,Tp,H,dk],
+    alpha_prev [B,Tp,H], dk_prev fp32 [B,Tp,H,dv]) -- the previous call's k, alpha and dk_out
+    and the accepted prefix lengths. Returns (o, dk_out)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", (B, T, H, dk), _ACT)
+    _need(k, "k", (B, T, H, dk), (q.dtype,))
+    _need(v, "v", (B, T, H, dv), (q.dtype,))
+    _need(alpha, "alpha", (B, T, H), (torch.float32,))
+    _need(beta, "beta", (B, T, H), (torch.float32,))
+    _need(state, "state", (B, H, dv, dk), _ACT)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    if dk_out is None:
+        dk_out = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", (B, T, H, dv), (q.dtype,))
+    _need(dk_out, "dk_out", (B, T, H, dv), (torch.float32,))
+    Tp, n_prev, k_prev, alpha_prev, dk_prev = 0, None, None, None, None
+    if prev is not None:
+        n_prev, k_prev, alpha_prev, dk_prev = prev
+        Tp = k_prev.shape[1]
+        _need(n_prev, "n_prev", (B,), (torch.int32,))
+        _need(k_prev, "k_prev", (B, Tp, H, dk), (q.dtype,))
+        _need(alpha_prev, "alpha_prev", (B, Tp, H), (torch.float32,))
+        _need(dk_prev, "dk_prev", (B, Tp, H, dv), (torch.float32,))
+    check(lib().gdn_decode_verify(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                  _DTYPE_CODE[q.dtype], _ptr(alpha), _ptr(beta), _ptr(state),
+                                  _DTYPE_CODE[state.dtype], Tp, _ptr(n_prev), _ptr(k_prev),
+                                  _ptr(alpha_prev), _ptr(dk_prev), _ptr(o), _ptr(dk_out),
+                                  float(scale), _stream(q.device)))
+    return o, dk_out
 
 
 def conv_gate_decode(qkv, conv_state, conv_w, conv_b, a_logit, b_logit, state, o=None,

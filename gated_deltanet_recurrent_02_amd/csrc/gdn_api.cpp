@@ -182,6 +182,64 @@ gdn_status gdn_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t 
     return GDN_OK;
 }
 
+gdn_status gdn_decode_verify(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                             const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                             const float* alpha, const float* beta,
+                             void* state, gdn_dtype state_dtype,
+                             int32_t Tp, const int32_t* n_prev, const void* k_prev,
+                             const float* alpha_prev, const float* dk_prev,
+                             void* o, float* dk_out, float scale, void* stream) {
+    static const char* fn = "gdn_decode_verify";
+    g_last_error.clear();
+    gdn_status s = check_shape(fn, B, T, H, dk, dv);
+    if (s != GDN_OK) return s;
+    if (Tp < 0) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": Tp must be >= 0");
+    if (!valid_dtype(act_dtype) || !valid_dtype(state_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": bad dtype");
+    if (B == 0 || (T == 0 && Tp == 0)) return GDN_OK;
+    s = check_ptrs(fn, {{"state", state}});
+    if (s != GDN_OK) return s;
+    if (T > 0) {
+        s = check_ptrs(fn, {{"q", q}, {"k", k}, {"v", v}, {"alpha", alpha}, {"beta", beta},
+                            {"o", o}, {"dk_out", dk_out}});
+        if (s != GDN_OK) return s;
+    }
+    if (Tp > 0) {
+        s = check_ptrs(fn, {{"n_prev", n_prev}, {"k_prev", k_prev}, {"alpha_prev", alpha_prev},
+                            {"dk_prev", dk_prev}});
+        if (s != GDN_OK) return s;
+    }
+    const size_t ab = dtype_bytes(act_dtype);
+    const size_t tok = (size_t)B * T * H, tokp = (size_t)B * Tp * H;
+    const size_t state_bytes = (size_t)B * H * dk * dv * dtype_bytes(state_dtype);
+    const Range r_s = range("state", state, state_bytes);
+    const Range r_q = range("q", q, tok * dk * ab), r_k = range("k", k, tok * dk * ab);
+    const Range r_v = range("v", v, tok * dv * ab), r_a = range("alpha", alpha, tok * 4);
+    const Range r_b = range("beta", beta, tok * 4), r_o = range("o", o, tok * dv * ab);
+    const Range r_d = range("dk_out", dk_out, tok * dv * 4);
+    const Range r_n = range("n_prev", n_prev, Tp > 0 ? (size_t)B * 4 : 0);
+    const Range r_kp = range("k_prev", k_prev, tokp * dk * ab);
+    const Range r_ap = range("alpha_prev", alpha_prev, tokp * 4);
+    const Range r_dp = range("dk_prev", dk_prev, tokp * dv * 4);
+    s = check_disjoint(fn, r_o, {r_s, r_q, r_k, r_v, r_a, r_b, r_d, r_n, r_kp, r_ap, r_dp});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_d, {r_s, r_q, r_k, r_v, r_a, r_b, r_n, r_kp, r_ap, r_dp});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_s, {r_q, r_k, r_v, r_a, r_b, r_n, r_kp, r_ap, r_dp});
+    if (s != GDN_OK) return s;
+
+    gdn::VerifyArgs a;
+    a.B = B; a.T = T; a.H = H; a.D = dk;
+    a.q = q; a.k = k; a.v = v; a.act = to_dtype(act_dtype);
+    a.alpha = alpha; a.beta = beta;
+    a.state = state; a.state_dtype = to_dtype(state_dtype);
+    a.Tp = Tp; a.n_prev = n_prev; a.k_prev = k_prev; a.alpha_prev = alpha_prev; a.dk_prev = dk_prev;
+    a.o = o; a.dk_out = dk_out; a.scale = scale;
+    hipError_t e = gdn::launch_verify(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip("gdn_decode_verify: kernel launch", e);
+    return GDN_OK;
+}
+
 gdn_status gdn_conv_gate_decode(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                                 const void* qkv, void* conv_state,
                                 const float* conv_w, const float* conv_b,

@@ -335,17 +335,22 @@ __device__ __forceinline__ float row_dots(const float (&S)[G::P][G::E], const fl
     return kq;
 }
 
+// What a token step returns on the lane with l == p of each row group, for the row of pass p:
+// its readout o and its write coefficient dk (the new state is alpha S + dk k_raw^T).
+struct RowOut {
+    float o, dk;
+};
+
 // One token with S held as is. k = kf k_raw, q = qf q_raw:
 //   u = kf (S k_raw);  delta = beta (v - alpha u);  S <- alpha S + (delta kf) k_raw;
 //   o = qf (alpha (S q_raw) + (delta kf) (k_raw . q_raw)).
-// Returns, on the lane with l == p of each row group, o of the row of pass p.
 template <class G>
-__device__ __forceinline__ float token_plain(float (&S)[G::P][G::E], const float (&kk)[G::E],
+__device__ __forceinline__ RowOut token_plain(float (&S)[G::P][G::E], const float (&kk)[G::E],
                                              const float (&qq)[G::E], const float (&vr)[G::P],
                                              float a, float bt, float kf, float qf, int l) {
     float u[G::P], w[G::P];
     const float kq = row_dots<G>(S, kk, qq, u, w);
-    float myo = 0.f;
+    RowOut r = {0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < G::P; ++p) {
         const float delta = bt * (vr[p] - a * (kf * u[p]));
@@ -353,9 +358,10 @@ __device__ __forceinline__ float token_plain(float (&S)[G::P][G::E], const float
 #pragma unroll
         for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(dk, kk[e], a * S[p][e]);
         const float op = qf * fmaf(a, w[p], dk * kq);
-        myo = (l == p) ? op : myo;
+        r.o = (l == p) ? op : r.o;
+        r.dk = (l == p) ? dk : r.dk;
     }
-    return myo;
+    return r;
 }
 
 // One token with registers holding S' = S / c; cn = c alpha (in [2^-64, 2^64]) is the new
@@ -364,14 +370,14 @@ __device__ __forceinline__ float token_plain(float (&S)[G::P][G::E], const float
 //   o = qf (cn w' + (delta kf) (k_raw . q_raw)),
 // since alpha S + dk k = cn (S' + dk k / cn) and alpha S q = cn S' q: one FMA per element.
 template <class G>
-__device__ __forceinline__ float token_scaled(float (&S)[G::P][G::E], const float (&kk)[G::E],
+__device__ __forceinline__ RowOut token_scaled(float (&S)[G::P][G::E], const float (&kk)[G::E],
                                               const float (&qq)[G::E], const float (&vr)[G::P],
                                               float a, float bt, float kf, float qf, float c,
                                               float cn, int l) {
     float u[G::P], w[G::P];
     const float kq = row_dots<G>(S, kk, qq, u, w);
     const float kc = kf * c, inv_cn = __builtin_amdgcn_rcpf(cn);
-    float myo = 0.f;
+    RowOut r = {0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < G::P; ++p) {
         const float delta = bt * (vr[p] - a * (kc * u[p]));
@@ -380,9 +386,10 @@ __device__ __forceinline__ float token_scaled(float (&S)[G::P][G::E], const floa
 #pragma unroll
         for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(coef, kk[e], S[p][e]);
         const float op = qf * fmaf(cn, w[p], dk * kq);
-        myo = (l == p) ? op : myo;
+        r.o = (l == p) ? op : r.o;
+        r.dk = (l == p) ? dk : r.dk;
     }
-    return myo;
+    return r;
 }
 
 template <class G>
@@ -432,14 +439,20 @@ struct TokenOperands {
 // With MULTI the registers hold S / c and `c` carries the scale across rounds: tokens run in
 // the scaled form while c alpha stays in [2^-64, 2^64]; a token that would leave that range
 // (alpha = 0, very small or large, NaN) folds c back into the registers and runs plainly.
-template <class G, bool MULTI, typename AT>
+// With DELTA, each token's write coefficients dk (one per row) also go to `dbase`, laid out
+// like o but in fp32.
+template <class G, bool MULTI, typename AT, bool DELTA = false>
 __device__ __forceinline__ void recur_tokens(float (&S)[G::P][G::E],
                                              const TokLds<G::D, G::TCH>& L, int nt, int rbase,
                                              int g, int l, AT* __restrict__ obase, size_t ostride,
-                                             float& c) {
+                                             float& c, float* __restrict__ dbase = nullptr) {
     const int row0 = rbase + g;
-    auto put_o = [&](int tt, float myo) {
-        if (l < G::P) obase[(size_t)tt * ostride + rbase + l * G::RPP + g] = act_from_f32<AT>(myo);
+    auto put_o = [&](int tt, RowOut r) {
+        if (l < G::P) {
+            const size_t at = (size_t)tt * ostride + rbase + l * G::RPP + g;
+            obase[at] = act_from_f32<AT>(r.o);
+            if constexpr (DELTA) dbase[at] = r.dk;
+        }
     };
     if constexpr (!MULTI) {
         for (int tt = 0; tt < nt; ++tt) {
@@ -608,6 +621,81 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     store_state<G>(Sg, rbase + g, l, S);
 }
 
+// ------------------------------------------------------------------------ verify kernel
+
+// Speculative verify with a deferred commit. The stored state is the committed state as of the
+// start of the previous call; that call's accepted prefix (n_prev[b] of its Tp tokens, clamped
+// to [0, Tp]) is folded in first by replaying its updates from the write coefficients it
+// emitted,
+//     S <- alpha_t S + dk_t k_t^T      for t < n_prev[b],
+// and the result is stored (nothing is stored when the prefix is empty). The T new tokens then
+// run from it in registers, emitting o and dk for every token; the state after them is not
+// stored: the next call commits whichever prefix was accepted. One state read and at most one
+// state write per call, as for a plain step.
+template <class G, typename AT>
+__global__ __launch_bounds__(G::NT) void gdn_verify_kernel(
+    int T, int H, const AT* __restrict__ q, const AT* __restrict__ k, const AT* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta,
+    typename G::ST* __restrict__ state, int Tp, const int32_t* __restrict__ n_prev,
+    const AT* __restrict__ k_prev, const float* __restrict__ alpha_prev,
+    const float* __restrict__ dk_prev, AT* __restrict__ o, float* __restrict__ dk_out,
+    float scale) {
+    constexpr int D = G::D;
+    __shared__ TokLds<D, G::TCH> L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / G::LPR, l = lane % G::LPR;
+    const uint32_t tile = tile_index<G::XCD, G::SPLIT>(blockIdx.x, gridDim.x);
+    const int64_t n = tile / G::SPLIT;  // b * H + h
+    const int part = (int)(tile - n * G::SPLIT);
+    const int64_t b = n / H;
+    const int h = (int)(n - b * H);
+    typename G::ST* Sg = state + (size_t)n * D * D;
+    const int rbase = part * G::RPG + wave * G::RPW;
+    const int row0 = rbase + g;
+
+    TokenStage<G, AT> st;
+    if (T > 0) st.fetch(q, k, v, alpha, beta, b, T, H, h, part, 0, min(G::TCH, T), tid);
+
+    float S[G::P][G::E];
+    load_state<G>(Sg, row0, l, S);
+
+    // Commit the previous call's accepted prefix.
+    int np = 0;
+    if (Tp > 0) {
+        np = __builtin_amdgcn_readfirstlane(n_prev[b]);
+        np = np < 0 ? 0 : (np > Tp ? Tp : np);
+    }
+    for (int t = 0; t < np; ++t) {
+        const size_t tok = ((size_t)b * Tp + t) * H + h;
+        float kk[G::E], dl[G::P];
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) kk[e] = act_to_f32(k_prev[tok * D + G::col(l, e)]);
+#pragma unroll
+        for (int p = 0; p < G::P; ++p) dl[p] = dk_prev[tok * D + row0 + p * G::RPP];
+        const float a = uniform(alpha_prev[tok]);
+#pragma unroll
+        for (int p = 0; p < G::P; ++p)
+#pragma unroll
+            for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(dl[p], kk[e], a * S[p][e]);
+    }
+    if (np > 0) store_state<G>(Sg, row0, l, S);
+
+    // Verify the new tokens from the committed state.
+    float c = 1.0f;
+    for (int t0 = 0; t0 < T; t0 += G::TCH) {
+        const int nt = min(G::TCH, T - t0);
+        if (t0 > 0) {
+            __syncthreads();  // the previous round's readers are done with L
+            st.fetch(q, k, v, alpha, beta, b, T, H, h, part, t0, nt, tid);
+        }
+        st.commit(L, part, nt, tid, scale);
+        __syncthreads();
+        const size_t ob = (((size_t)b * T + t0) * H + h) * D;
+        recur_tokens<G, true, AT, true>(S, L, nt, rbase, g, l, o + ob, (size_t)H * D, c,
+                                        dk_out + ob);
+    }
+}
+
 // ------------------------------------------------------------------------ fused kernel
 
 // One workgroup per head (SPLIT == 1): it is then the only reader and writer of the head's
@@ -757,6 +845,28 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
                            dim3((unsigned)(a.B * a.H * G::SPLIT)), dim3(G::NT), args, 0, s);
 }
 
+template <class G, typename AT>
+hipError_t launch_verify_g(const VerifyArgs& a, hipStream_t s) {
+    int T = a.T, H = a.H, Tp = a.Tp;
+    const AT* q = (const AT*)a.q;
+    const AT* k = (const AT*)a.k;
+    const AT* v = (const AT*)a.v;
+    const float* alpha = a.alpha;
+    const float* beta = a.beta;
+    typename G::ST* state = (typename G::ST*)a.state;
+    const int32_t* n_prev = a.n_prev;
+    const AT* k_prev = (const AT*)a.k_prev;
+    const float* alpha_prev = a.alpha_prev;
+    const float* dk_prev = a.dk_prev;
+    AT* o = (AT*)a.o;
+    float* dk_out = a.dk_out;
+    float scale = a.scale;
+    void* args[] = {&T, &H, &q, &k, &v, &alpha, &beta, &state, &Tp, &n_prev, &k_prev,
+                    &alpha_prev, &dk_prev, &o, &dk_out, &scale};
+    return hipLaunchKernel((const void*)gdn_verify_kernel<G, AT>,
+                           dim3((unsigned)(a.B * a.H * G::SPLIT)), dim3(G::NT), args, 0, s);
+}
+
 template <class G, bool MULTI>
 hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
     int T = a.T, H = a.H;
@@ -828,6 +938,25 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
 }
 
 template <int D, typename ST>
+hipError_t launch_verify_s(const VerifyArgs& a, hipStream_t s) {
+    using G = typename DecodeTokens<D, ST>::G;
+    switch (a.act) {
+        case DType::F32: return launch_verify_g<G, float>(a, s);
+        case DType::BF16: return launch_verify_g<G, uint16_t>(a, s);
+        default: return launch_verify_g<G, _Float16>(a, s);
+    }
+}
+
+template <int D>
+hipError_t launch_verify_d(const VerifyArgs& a, hipStream_t s) {
+    switch (a.state_dtype) {
+        case DType::F32: return launch_verify_s<D, float>(a, s);
+        case DType::BF16: return launch_verify_s<D, uint16_t>(a, s);
+        default: return launch_verify_s<D, _Float16>(a, s);
+    }
+}
+
+template <int D, typename ST>
 hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
     if (a.T == 1) return launch_fused_g<typename FusedTokens<D, ST>::G, false>(a, s);
     return launch_fused_g<typename FusedTokens<D, ST>::G, true>(a, s);
@@ -850,6 +979,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
         case 32: return launch_decode_d<32>(a, s);
         case 64: return launch_decode_d<64>(a, s);
         case 128: return launch_decode_d<128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
+    switch (a.D) {
+        case 16: return launch_verify_d<16>(a, s);
+        case 32: return launch_verify_d<32>(a, s);
+        case 64: return launch_verify_d<64>(a, s);
+        case 128: return launch_verify_d<128>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

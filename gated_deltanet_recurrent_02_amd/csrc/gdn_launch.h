@@ -41,8 +41,30 @@ struct FusedArgs {
     float l2_eps;
 };
 
-// Both return hipSuccess or the launch error; nothing is synchronised.
+struct VerifyArgs {
+    int64_t B;
+    int32_t T, H, D;          // T new tokens (may be 0: commit only)
+    const void* q;            // act [B][T][H][D]
+    const void* k;
+    const void* v;
+    DType act;
+    const float* alpha;       // [B][T][H]
+    const float* beta;
+    void* state;              // state dtype [B][H][D][D]
+    DType state_dtype;
+    int32_t Tp;               // tokens of the previous call (0: nothing to commit)
+    const int32_t* n_prev;    // [B] accepted prefix of the previous call (device)
+    const void* k_prev;       // act [B][Tp][H][D]
+    const float* alpha_prev;  // [B][Tp][H]
+    const float* dk_prev;     // [B][Tp][H][D] write coefficients emitted by the previous call
+    void* o;                  // act [B][T][H][D]
+    float* dk_out;            // [B][T][H][D]
+    float scale;
+};
+
+// All return hipSuccess or the launch error; nothing is synchronised.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_conv_gate_decode(const FusedArgs& a, hipStream_t stream);
 
 }  // namespace gdn

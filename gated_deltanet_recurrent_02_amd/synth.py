@@ -34,7 +34,18 @@ WORKLOADS = {
     "decode_b256_h48_d128_t1": dict(B=256, H=48, D=128, T=1, act="bf16", state_init="normal"),
     "decode_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, act="bf16", state_init="normal"),
     "fused_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, fused=True),
+    # speculative verify rounds of 4 tokens; the accepted prefix per sequence is drawn by
+    # accepted_prefix() below
+    "verify_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, act="bf16", state_init="normal",
+                                    verify=True),
 }
+
+
+def accepted_prefix(B: int, T: int, seed: int = 0) -> torch.Tensor:
+    """Accepted draft-prefix lengths per sequence for verify rounds: uniform on [1, T] (the
+    pages give no acceptance rates), int32 [B]."""
+    rng = _rng(seed + 1)
+    return torch.from_numpy(rng.integers(1, T + 1, B).astype(np.int32))
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -104,6 +115,7 @@ def workload_inputs(name: str, *, seed: int = 0, **overrides) -> dict:
     """Inputs of a named workload (see WORKLOADS); keyword overrides replace recipe fields."""
     spec = dict(WORKLOADS[name])
     fused = spec.pop("fused", False)
+    spec.pop("verify", False)
     spec.update(overrides)
     if fused:
         return fused_inputs(seed=seed, **spec)

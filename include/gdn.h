@@ -102,6 +102,44 @@ gdn_status gdn_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t 
                            void* o, float scale, void* stream);
 
 /*
+ * gdn_decode_verify — speculative / multi-token-prediction verify with a deferred commit of the
+ * accepted prefix (for decoding that checks T drafted tokens in one pass and keeps only a
+ * prefix of them; "GDN tuning limits on Kunlun XPU", sections 三.2 and 四, run GDN under MTP).
+ * The pages do not define how the recurrent state drops rejected tokens; this is the reading:
+ *
+ *   1. `state` holds the committed state as of the start of the previous verify call. That call
+ *      had Tp tokens; n_prev[b] (clamped to [0, Tp]) of them were accepted for sequence b. They
+ *      are committed by replaying their updates, S <- alpha_t S + dk_t k_t^T for t < n_prev[b],
+ *      from the previous call's keys, decays and emitted write coefficients; the result is
+ *      stored in `state` (left untouched where the prefix is empty).
+ *   2. The T new tokens run from that committed state exactly as in gdn_decode_step, writing o
+ *      for every token and their write coefficients dk_out (dk_t = beta_t (v_t - alpha_t S k_t),
+ *      so that S_t = alpha_t S_{t-1} + dk_t k_t^T); the state after them is NOT stored.
+ *
+ * A first call passes Tp = 0; a final call that only commits passes T = 0. The caller keeps
+ * each call's k, alpha and dk_out for the next call. One state read and at most one state
+ * write per call, as for gdn_decode_step.
+ *
+ *   q, k, v, alpha, beta, o, scale  as gdn_decode_step, for the T new tokens
+ *   state       state_dtype [B][H][dv][dk], read; written with the committed state
+ *   Tp          tokens of the previous call (>= 0)
+ *   n_prev      int32 [B], device; accepted prefix length per sequence (clamped to [0, Tp])
+ *   k_prev      act_dtype [B][Tp][H][dk], the previous call's k
+ *   alpha_prev  fp32 [B][Tp][H], the previous call's alpha
+ *   dk_prev     fp32 [B][Tp][H][dv], the previous call's dk_out
+ *   dk_out      fp32 [B][T][H][dv], written; must not overlap any other argument (nor o)
+ * Pointers of an empty part (T == 0, or Tp == 0) may be NULL.
+ * Errors: as gdn_decode_step.
+ */
+gdn_status gdn_decode_verify(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                             const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                             const float* alpha, const float* beta,
+                             void* state, gdn_dtype state_dtype,
+                             int32_t Tp, const int32_t* n_prev, const void* k_prev,
+                             const float* alpha_prev, const float* dk_prev,
+                             void* o, float* dk_out, float scale, void* stream);
+
+/*
  * gdn_conv_gate_decode — the fused layer path of the same chain ("GDN tuning limits on Kunlun
  * XPU", section 二: short causal conv of kernel size 4, then gating, then the recurrent
  * update), for T sequential tokens:

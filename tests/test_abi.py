@@ -184,3 +184,45 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 1, 16)
     with pytest.raises(ValueError, match="HIP device"):
         gdn.decode_step(q, q, q, torch.zeros(1, 1, 1), torch.zeros(1, 1, 1), torch.zeros(1, 1, 16, 16))
+
+
+def verify(B=2, T=2, H=4, D=16, Tp=2, n_prev=None, k_prev=None, a_prev=None, d_prev=None,
+           o=None, dk_out=None, state=None, q=None):
+    L = gdn.lib()
+    q = P(0) if q is None else q
+    state = P(80 * MB) if state is None else state
+    n_prev = P(200 * MB) if n_prev is None else n_prev
+    k_prev = P(210 * MB) if k_prev is None else k_prev
+    a_prev = P(220 * MB) if a_prev is None else a_prev
+    d_prev = P(230 * MB) if d_prev is None else d_prev
+    o = P(160 * MB) if o is None else o
+    dk_out = P(170 * MB) if dk_out is None else dk_out
+    return L.gdn_decode_verify(B, T, H, D, D, q, P(16 * MB), P(32 * MB), F32, P(48 * MB),
+                               P(64 * MB), state, F32, Tp, n_prev, k_prev, a_prev, d_prev, o,
+                               dk_out, 1.0, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Tp=-1), INVALID, "Tp must be"),
+    (dict(n_prev=ctypes.c_void_p(0)), INVALID, "n_prev is NULL"),
+    (dict(d_prev=P(230 * MB + 4)), INVALID, "dk_prev is not 16-byte aligned"),
+    (dict(dk_out=ctypes.c_void_p(0)), INVALID, "dk_out is NULL"),
+    (dict(dk_out=P(160 * MB + 64)), INVALID, "o overlaps dk_out"),
+    (dict(dk_out=P(230 * MB)), INVALID, "dk_out overlaps dk_prev"),
+    (dict(state=P(210 * MB)), INVALID, "state overlaps k_prev"),
+    (dict(D=48), UNSUPPORTED, "head dims"),
+])
+@fake_ptrs
+def test_decode_verify_rejects(kw, status, msg):
+    assert verify(**kw) == status
+    assert msg in last_error()
+
+
+@fake_ptrs
+def test_decode_verify_empty_parts_may_be_null():
+    N = ctypes.c_void_p(0)
+    # nothing to commit and nothing new: a no-op even with every pointer NULL
+    assert gdn.lib().gdn_decode_verify(2, 0, 4, 16, 16, N, N, N, F32, N, N, N, F32, 0, N, N, N, N,
+                                       N, N, 1.0, None) == 0
+    # commit only (T = 0): new-token pointers may be NULL; passes validation, fails at launch
+    assert verify(T=0, q=N, o=N, dk_out=N) == HIP
