@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "GDN decode µs/layer + achieved HBM GB/s (% roofline), B=256 H=48 128×128"
 DEFAULT_WORKLOAD = "decode_b256_h48_d128_t1"
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP32_MFMA_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_deltanet_recurrent_02_amd", "csrc", f)
@@ -62,6 +63,8 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
     ap.add_argument("--graph-groups", type=int, default=7, help="graph-replay groups (0 = skip)")
     ap.add_argument("--graph-replays", type=int, default=400, help="launches per graph replay")
+    ap.add_argument("--sequential", action="store_true",
+                    help="prompt workloads: time gdn_decode_step (token by token) instead of gdn_prefill")
     return ap.parse_args(argv)
 
 
@@ -132,10 +135,11 @@ def time_gpu(args, spec, workload):
     x = synth.workload_inputs(workload, state_dtype=args.state_dtype)
     x_B, x_T = x["B"], x["T"]
     state_bytes = x["state"].numel() * x["state"].element_size()
-    L = args.layers or max(1, math.ceil(2 * MALL_BYTES / state_bytes))
+    layer_bytes = sum(v.numel() * v.element_size() for v in x.values() if isinstance(v, torch.Tensor))
+    L = args.layers or max(1, math.ceil(2 * MALL_BYTES / layer_bytes))
     L = min(L, 64)
     print(f"[bench] {workload} state={args.state_dtype} layers={L} "
-          f"state_bytes={state_bytes}", file=sys.stderr, flush=True)
+          f"state_bytes={state_bytes} layer_bytes={layer_bytes}", file=sys.stderr, flush=True)
     layers = []
     for i in range(L):
         g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
@@ -161,6 +165,12 @@ def time_gpu(args, spec, workload):
                               prev=(n_acc, g["k"], g["alpha"], g["dk"][1 - j]), o=g["o"],
                               dk_out=g["dk"][j])
             g["i"] += 1
+    elif spec.get("prefill") and not args.sequential:
+        ws = gdn.prefill_workspace(layers[0]["q"], layers[0]["v"])  # launches are serialised
+
+        def step(g):
+            gdn.prefill(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state"], o=g["o"],
+                        workspace=ws)
     elif fused:
         def step(g):
             gdn.conv_gate_decode(g["qkv"], g["conv_state"], g["conv_w"], g["conv_b"], g["a_logit"],
@@ -253,7 +263,10 @@ def cpu_baseline(spec: dict, workload: str, state_dtype: str, target_s: float):
 
     B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
     Bs = max(1, min(B, 8))
-    x = synth.workload_inputs(workload, state_dtype=state_dtype, B=Bs)
+    Ts = T
+    if spec.get("prefill"):  # the oracle's time is linear in T: a prefix of one prompt
+        Bs, Ts = 1, min(T, 256)
+    x = synth.workload_inputs(workload, state_dtype=state_dtype, B=Bs, T=Ts)
     f = lambda t: t.double().numpy()
     if spec.get("fused"):
         args = (f(x["qkv"]), f(x["conv_state"]), f(x["conv_w"]), None, f(x["a_logit"]),
@@ -272,10 +285,11 @@ def cpu_baseline(spec: dict, workload: str, state_dtype: str, target_s: float):
         if el >= target_s:
             break
     per_rep = el / reps
-    us_per_layer = per_rep * (B / Bs) * 1e6
+    us_per_layer = per_rep * (B / Bs) * (T / Ts) * 1e6
+    scaled = f"{B}/{Bs}" + (f" x {T}/{Ts} tokens" if Ts != T else "")
     return {"value": us_per_layer, "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": f"{Bs} of {B} sequences x {H} heads (D={D}, T={T}), fp64 single-thread C "
-                      f"oracle, {reps} repetitions in {el:.1f} s, scaled by {B}/{Bs}",
+            "sample": f"{Bs} of {B} sequences x {H} heads (D={D}, T={Ts} of {T}), fp64 "
+                      f"single-thread C oracle, {reps} repetitions in {el:.1f} s, scaled by {scaled}",
             "host_cpus": os.cpu_count()}
 
 
@@ -317,7 +331,9 @@ def main(argv=None):
         "config": {"workload": args.workload, "B": B, "H": H, "dk": D, "dv": D, "T": T,
                    "state_dtype": args.state_dtype, "act_dtype": act,
                    "entry_point": ("gdn_conv_gate_decode" if spec.get("fused") else
-                                   "gdn_decode_verify" if spec.get("verify") else "gdn_decode_step"),
+                                   "gdn_decode_verify" if spec.get("verify") else
+                                   "gdn_prefill" if spec.get("prefill") and not args.sequential else
+                                   "gdn_decode_step"),
                    "layers_rotated": L},
         "achieved_gbps": gbps,
         "seq_tokens_per_s": B * T / (ms * 1e-3),
@@ -330,6 +346,16 @@ def main(argv=None):
     }
     line.update(extra)
     line["frac_of_copy_bw"] = gbps / extra["copy_gbps_same_bytes"]
+    if spec.get("prefill") and not args.sequential:
+        # The chunked form is bound by fp32 matrix-core arithmetic, not by HBM: price the
+        # recurrence's flops (per token and head: S k, S q and the rank-1 update, 6 D^2) against
+        # the fp32 MFMA peak. The time is the whole call (prep kernel + state kernel).
+        tf = flops(spec) / (ms * 1e-3) / 1e12
+        line["roofline_hbm"] = line["roofline"]
+        line["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS,
+                            "unit": "TFLOP/s", "frac": tf / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                            "algorithmic_flops_per_launch": flops(spec),
+                            "timed": "whole gdn_prefill call (prep + state kernels)"}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(spec, args.workload, args.state_dtype, args.cpu_seconds)

@@ -21,7 +21,8 @@ _CODE_DTYPE = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16, GDN_F16: torch.
 
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_state_alloc", "gdn_state_free", "gdn_decode_step", "gdn_decode_verify",
-           "gdn_conv_gate_decode", "gdn_status_string", "gdn_last_error")
+           "gdn_conv_gate_decode", "gdn_prefill_workspace_size", "gdn_prefill",
+           "gdn_status_string", "gdn_last_error")
 
 
 class GDNError(RuntimeError):
@@ -60,6 +61,11 @@ def _declare(L):
     L.gdn_decode_verify.restype = i
     L.gdn_conv_gate_decode.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, i, P, f32, f32, P]
     L.gdn_conv_gate_decode.restype = i
+    L.gdn_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.gdn_prefill_workspace_size.restype = i
+    L.gdn_prefill.argtypes = [i64, i32, i32, i32, i32, P, P, P, i, P, P, P, i, P, f32, P,
+                              ctypes.c_size_t, P]
+    L.gdn_prefill.restype = i
     L.gdn_status_string.argtypes = [i]
     L.gdn_status_string.restype = ctypes.c_char_p
     L.gdn_last_error.argtypes = []
@@ -119,6 +125,46 @@ def decode_step(q, k, v, alpha, beta, state, o=None, scale: float = 1.0):
     check(lib().gdn_decode_step(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype],
                                 _ptr(alpha), _ptr(beta), _ptr(state), _DTYPE_CODE[state.dtype],
                                 _ptr(o), float(scale), _stream(q.device)))
+    return o
+
+
+def prefill_workspace_size(B: int, T: int, H: int, dk: int, dv: int) -> int:
+    """gdn_prefill_workspace_size: bytes of workspace gdn_prefill needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    check(lib().gdn_prefill_workspace_size(B, T, H, dk, dv, ctypes.byref(n)))
+    return n.value
+
+
+def prefill_workspace(q, v) -> torch.Tensor:
+    """A uint8 device buffer of the workspace size for these q [B,T,H,dk] and v [..,dv]."""
+    B, T, H, dk = q.shape
+    n = prefill_workspace_size(B, T, H, dk, v.shape[-1])
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+
+
+def prefill(q, k, v, alpha, beta, state, o=None, scale: float = 1.0, workspace=None):
+    """gdn_prefill on torch tensors: the arguments and result of decode_step, computed in the
+    chunked form; updates `state` in place and returns o. `workspace` (optional) is a device
+    buffer of at least prefill_workspace_size(...) bytes; one is allocated when omitted."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", (B, T, H, dk), _ACT)
+    _need(k, "k", (B, T, H, dk), (q.dtype,))
+    _need(v, "v", (B, T, H, dv), (q.dtype,))
+    _need(alpha, "alpha", (B, T, H), (torch.float32,))
+    _need(beta, "beta", (B, T, H), (torch.float32,))
+    _need(state, "state", (B, H, dv, dk), _ACT)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    _need(o, "o", (B, T, H, dv), (q.dtype,))
+    if workspace is None:
+        workspace = prefill_workspace(q, v)
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    check(lib().gdn_prefill(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype],
+                            _ptr(alpha), _ptr(beta), _ptr(state), _DTYPE_CODE[state.dtype],
+                            _ptr(o), float(scale), _ptr(workspace), nbytes, _stream(q.device)))
     return o
 
 

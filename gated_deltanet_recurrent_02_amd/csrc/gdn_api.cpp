@@ -11,6 +11,7 @@
 #include <string>
 
 #include "gdn_launch.h"
+#include "gdn_prefill_launch.h"
 
 namespace {
 
@@ -285,6 +286,83 @@ gdn_status gdn_conv_gate_decode(int64_t B, int32_t T, int32_t H, int32_t dk, int
     a.o = o; a.scale = scale; a.l2_eps = l2_eps;
     hipError_t e = gdn::launch_conv_gate_decode(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip("gdn_conv_gate_decode: kernel launch", e);
+    return GDN_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace bytes of gdn_prefill; false if the size overflows size_t.
+bool prefill_ws_bytes(int64_t B, int32_t T, int32_t H, size_t* out) {
+    size_t n = 0;
+    return mul_ok((size_t)B, (size_t)H, &n) && mul_ok(n, (size_t)gdn::prefill_chunks(T), &n) &&
+           mul_ok(n, (size_t)gdn::kPrefillRecordFloats * sizeof(float), out);
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_workspace_size(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                      size_t* bytes) {
+    static const char* fn = "gdn_prefill_workspace_size";
+    g_last_error.clear();
+    if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": bytes is NULL");
+    *bytes = 0;
+    gdn_status s = check_shape(fn, B, T, H, dk, dv);
+    if (s != GDN_OK) return s;
+    if (!prefill_ws_bytes(B, T, H, bytes)) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": size overflows");
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                       const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                       const float* alpha, const float* beta,
+                       void* state, gdn_dtype state_dtype,
+                       void* o, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    static const char* fn = "gdn_prefill";
+    g_last_error.clear();
+    gdn_status s = check_shape(fn, B, T, H, dk, dv);
+    if (s != GDN_OK) return s;
+    if (!valid_dtype(act_dtype) || !valid_dtype(state_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": bad dtype");
+    if (B == 0 || T == 0) return GDN_OK;
+    if (B * (int64_t)H * gdn::prefill_chunks(T) >= (int64_t(1) << 31))
+        return fail(GDN_ERR_UNSUPPORTED, std::string(fn) + ": B * H * ceil(T / 16) must be < 2^31");
+    s = check_ptrs(fn, {{"q", q}, {"k", k}, {"v", v}, {"alpha", alpha}, {"beta", beta},
+                        {"state", state}, {"o", o}, {"workspace", workspace}});
+    if (s != GDN_OK) return s;
+    size_t need = 0;
+    if (!prefill_ws_bytes(B, T, H, &need)) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": size overflows");
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": workspace has " +
+                                                  std::to_string(workspace_bytes) + " bytes, " +
+                                                  std::to_string(need) + " needed");
+    const size_t tokens = (size_t)B * T * H;
+    const size_t ab = dtype_bytes(act_dtype);
+    const size_t state_bytes = (size_t)B * H * dk * dv * dtype_bytes(state_dtype);
+    const Range r_q = range("q", q, tokens * dk * ab), r_k = range("k", k, tokens * dk * ab);
+    const Range r_v = range("v", v, tokens * dv * ab), r_a = range("alpha", alpha, tokens * 4);
+    const Range r_b = range("beta", beta, tokens * 4), r_s = range("state", state, state_bytes);
+    const Range r_o = range("o", o, tokens * dv * ab), r_w = range("workspace", workspace, need);
+    s = check_disjoint(fn, r_o, {r_q, r_k, r_v, r_a, r_b, r_s, r_w});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_s, {r_q, r_k, r_v, r_a, r_b, r_w});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_w, {r_q, r_k, r_v, r_a, r_b});
+    if (s != GDN_OK) return s;
+
+    gdn::PrefillArgs a;
+    a.B = B; a.T = T; a.H = H; a.D = dk;
+    a.q = q; a.k = k; a.v = v; a.act = to_dtype(act_dtype);
+    a.alpha = alpha; a.beta = beta;
+    a.state = state; a.state_dtype = to_dtype(state_dtype);
+    a.o = o; a.scale = scale;
+    a.ws = static_cast<float*>(workspace);
+    hipError_t e = gdn::launch_prefill(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip("gdn_prefill: kernel launch", e);
     return GDN_OK;
 }
 

@@ -1,0 +1,450 @@
+// Chunked (prefill) form of the gated delta rule on gfx950 (CDNA4): T sequential tokens per
+// head with the state-touching work done as dense products on the matrix cores.
+//
+// The result is that of T steps of the recurrence ("GDN tuning limits on Kunlun XPU", section
+// 二: S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t (scale q_t)); the
+// same page (section 三.3) runs long prompts through a chunked form of it. Regrouping over a chunk
+// of 16 tokens t = 0..15 with S the state before the chunk and
+//     gamma_t = alpha_0 alpha_1 ... alpha_t,   Gam_ts = alpha_{s+1} ... alpha_t  (Gam_tt = 1),
+// and the kernel form delta_t = beta_t (v_t - alpha_t S_{t-1} k_t), S_t = alpha_t S_{t-1} + delta_t k_t^T:
+//     S_t = gamma_t S + sum_{s<=t} Gam_ts delta_s k_s^T, so (I + A) Delta = diag(beta) (V - gamma . K S^T)
+// with A_ts = beta_t Gam_ts (k_t . k_s) for s < t (strictly lower triangular), Delta the 16 x dv
+// matrix of the delta_t, and
+//     Delta = T diag(beta) (V - gamma . X),   X = K S^T,            T = (I + A)^-1
+//     O     = scale gamma . (Q S^T) + P Delta,   P_ts = scale Gam_ts (q_t . k_s), s <= t
+//     S_end = gamma_15 S + Delta^T diag(Gam_end) K,   Gam_end,t = alpha_{t+1} ... alpha_15
+// (". " scales row t by the per-token factor). All decays are products of alphas, never ratios,
+// so alpha = 0 is exact. Tokens past the end of the sequence enter with alpha = 1, beta = 0 and
+// zero vectors, which makes their delta exactly 0.
+//
+// Two kernels:
+//   * prep (one wave per (b, h, chunk); all chunks in parallel): the chunk's Gram products
+//     K K^T and Q K^T on MFMA, the decays, T by forward substitution, written as one record of
+//     544 floats to the caller's workspace;
+//   * state (one wave per (b, h, 16 state rows), sequential over the chunks): the rows' state
+//     stays in registers for the whole call; per chunk five MFMA products (X, Q S^T, T diag(beta),
+//     P, the update), 104 v_mfma_f32_16x16x4f32 at D = 128, with the next chunk's operands
+//     loaded while the current one computes.
+// Matrix-core layout (v_mfma_f32_16x16x4f32, lane l = 16 g + n): operand a is A[l%16][l/16],
+// operand b is B[l/16][l%16], and the accumulator holds C[4 g + i][n], i = 0..3 (checked on the
+// device against a CPU product). The state's accumulator tiles of the update are arranged so that
+// the same registers are the b operand of the next chunk's K S^T and Q S^T: tile mt, element i
+// of lane (g, n) is S[row n][column (D/4) g + (D/16) i + mt], so each lane holds one state row's
+// contiguous run of D/4 columns and every load in the kernel is a contiguous vector.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_prefill_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int CH = kPrefillChunk;
+constexpr int REC = kPrefillRecordFloats;
+constexpr int REC_T = 0, REC_P = 256, REC_G = 512, REC_GE = 528;
+static_assert(REC == REC_GE + CH, "record layout");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// D += A B over one 4-wide slice of the contraction (16 x 16 x 4, fp32 in and out).
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Element types of activations and state: float, uint16_t (bf16 bits), _Float16.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float get(const uint32_t* w, int e) { return __uint_as_float(w[e]); }
+};
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float get(const uint32_t* w, int e) {
+        const uint32_t x = w[e >> 1];
+        return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+    }
+    // Round to nearest even (gfx950's v_cvt_pk_bf16_f32), NaN stays NaN.
+    static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+        const f32x2_t v = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    }
+};
+template <> struct Elem<_Float16> {
+    static __device__ __forceinline__ float get(const uint32_t* w, int e) {
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, w[e >> 1]);
+        return (float)((e & 1) ? h.y : h.x);
+    }
+    // Round to nearest even (v_cvt_pk_f16_f32).
+    static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+        const f32x2_t v = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    }
+};
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
+    return (uint16_t)(Elem<uint16_t>::pack(x, 0.0f) & 0xffffu);
+}
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) {
+    return __builtin_bit_cast(_Float16, (uint16_t)(Elem<_Float16>::pack(x, 0.0f) & 0xffffu));
+}
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+template <> __device__ __forceinline__ float to_f32<_Float16>(_Float16 x) { return (float)x; }
+
+// N contiguous elements of type T held as raw 32-bit words, loaded with the widest vector
+// accesses their alignment allows (a run of N elements starts at a multiple of min(16, bytes)).
+template <typename T, int N>
+struct Run {
+    static constexpr int BYTES = N * (int)sizeof(T);
+    static constexpr int WORDS = (BYTES + 3) / 4;
+    uint32_t w[WORDS];
+
+    template <bool NT = false>
+    __device__ __forceinline__ void load(const T* p) {
+        if constexpr (BYTES >= 16) {
+            static_assert(BYTES % 16 == 0, "run length");
+#pragma unroll
+            for (int i = 0; i < BYTES / 16; ++i) {
+                const u32x4* a = (const u32x4*)p + i;
+                const u32x4 x = NT ? __builtin_nontemporal_load(a) : *a;
+                w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+            }
+        } else if constexpr (BYTES == 8) {
+            const u32x2 x = *(const u32x2*)p;
+            w[0] = x.x; w[1] = x.y;
+        } else if constexpr (BYTES == 4) {
+            w[0] = *(const uint32_t*)p;
+        } else {
+            static_assert(BYTES == 2, "run length");
+            w[0] = *(const uint16_t*)p;
+        }
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < WORDS; ++i) w[i] = 0u;
+    }
+    __device__ __forceinline__ float get(int e) const { return Elem<T>::get(w, e); }
+};
+
+// Stores N floats as N contiguous elements of T (rounded to nearest even for 2-byte types).
+template <typename T, int N, bool NT>
+__device__ __forceinline__ void store_run(T* p, const float* x) {
+    constexpr int BYTES = N * (int)sizeof(T);
+    uint32_t w[(BYTES + 3) / 4];
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) w[e] = __float_as_uint(x[e]);
+    } else {
+        static_assert(N % 2 == 0, "run length");
+#pragma unroll
+        for (int e = 0; e < N; e += 2) w[e / 2] = Elem<T>::pack(x[e], x[e + 1]);
+    }
+    static_assert(BYTES % 16 == 0 || BYTES == 8, "run length");
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+        for (int i = 0; i < BYTES / 16; ++i) {
+            const u32x4 v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            if (NT) __builtin_nontemporal_store(v, (u32x4*)p + i); else ((u32x4*)p)[i] = v;
+        }
+    } else {
+        const u32x2 v = {w[0], w[1]};
+        *(u32x2*)p = v;
+    }
+}
+
+// ------------------------------------------------------------------------ prep kernel
+
+// One wave per (b, h, chunk c); workgroup id = (b H + h) nch + c, which is also the record's
+// index in the workspace. Lane (g, n) = (lane / 16, lane % 16) holds token n's q and k over the
+// columns (D/4) g .. (D/4) g + D/4 - 1, so that the same registers are the a and b operands of
+// the Gram products (the contraction runs over the key dim in any order).
+template <int D, typename AT>
+__global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
+    int T, int H, int nch, const AT* __restrict__ q, const AT* __restrict__ k,
+    const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ ws,
+    float scale) {
+    constexpr int R = D / 4;
+    __shared__ float sA[CH][CH];
+    const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
+    const uint32_t wid = blockIdx.x;
+    const int c = (int)(wid % (uint32_t)nch);
+    const int64_t bh = wid / (uint32_t)nch;
+    const int64_t b = bh / H;
+    const int h = (int)(bh % H);
+    const int t0 = c * CH;
+    const int nv = min(CH, T - t0);
+
+    Run<AT, R> kx, qx;
+    if (n < nv) {
+        const int64_t off = ((b * T + t0 + n) * H + h) * D + R * g;
+        kx.load(k + off);
+        qx.load(q + off);
+    } else {
+        kx.zero();
+        qx.zero();
+    }
+    // Lane t < 16 holds token t's gates; past the end alpha = 1, beta = 0.
+    float al = 1.0f, be = 0.0f;
+    if (lane < nv) {
+        const int64_t ti = (b * T + t0 + lane) * H + h;
+        al = alpha[ti];
+        be = beta[ti];
+    }
+
+    // G[t][s] = k_t . k_s and QK[t][s] = q_t . k_s; lane (g, n) holds rows t = 4g + j, column s = n.
+    f32x4 G = {0.f, 0.f, 0.f, 0.f}, QK = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+        const float ke = kx.get(e);
+        G = mfma4(ke, ke, G);
+        QK = mfma4(qx.get(e), ke, QK);
+    }
+
+    // Gam_ts for t = 4g + j, s = n: the product of alpha_r over s < r <= t (1 if empty), in
+    // increasing r; gamma_l = alpha_0 ... alpha_l and Gam_end,l = alpha_{l+1} ... alpha_15 for
+    // the lane's own token l = lane (lanes < 16).
+    float gam[4] = {1.f, 1.f, 1.f, 1.f};
+    float gl = 1.0f, ge = 1.0f;
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+        const float ar = lane_value(al, r);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (r > n && r <= 4 * g + j) gam[j] *= ar;
+        if (r <= lane) gl *= ar; else ge *= ar;
+    }
+
+    float* rec = ws + (size_t)wid * REC;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = 4 * g + j;
+        const float bt = __shfl(be, t);
+        sA[t][n] = (n < t) ? bt * gam[j] * G[j] : 0.0f;
+        rec[REC_P + t * CH + n] = (n <= t) ? scale * gam[j] * QK[j] : 0.0f;
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1 by forward substitution: lane c < 16 computes column c,
+    // T[t][c] = [t == c] - sum_{s<t} A[t][s] T[s][c]; stored with column c scaled by beta_c.
+    if (lane < CH) {
+        float x[CH];
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+            float acc = (t == lane) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int s = 0; s < t; ++s) acc = fmaf(-sA[t][s], x[s], acc);
+            x[t] = acc;
+        }
+#pragma unroll
+        for (int t = 0; t < CH; ++t) rec[REC_T + t * CH + lane] = x[t] * be;
+        rec[REC_G + lane] = gl;
+        rec[REC_GE + lane] = ge;
+    }
+}
+
+// ------------------------------------------------------------------------ state kernel
+
+// One lane's operands of one chunk: lane (g, m) = (lane / 16, lane % 16).
+template <int D, typename AT>
+struct ChunkOps {
+    static constexpr int R = D / 4, NMT = D / 16;
+    Run<AT, R> kx, qx;   // a operands of K S^T and Q S^T: token m, columns R g .. R g + R - 1
+    Run<AT, NMT> ku[4];  // a operand of the update, step s: token 4g + s, columns NMT m .. + NMT
+    float v[4];          // v[token 4g + j][state row]
+    f32x4 tb, pm;        // T diag(beta)[m][4g .. 4g+3], P[m][4g .. 4g+3]
+    f32x4 gm, ge;        // gamma and Gam_end of tokens 4g .. 4g+3
+    float gend;          // gamma_15: decay of the whole chunk
+};
+
+template <int D, typename AT>
+__device__ __forceinline__ void load_chunk(ChunkOps<D, AT>& x, int c, int T, int H, int64_t b,
+                                           int h, int row, const AT* __restrict__ q,
+                                           const AT* __restrict__ k, const AT* __restrict__ v,
+                                           const float* __restrict__ wsh, int g, int m) {
+    constexpr int R = D / 4, NMT = D / 16;
+    const int t0 = c * CH;
+    const int nv = min(CH, T - t0);
+    const int64_t tok0 = (b * T + t0) * H + h;  // index of (b, t0, h) in [B][T][H]
+    if (m < nv) {
+        const int64_t off = (tok0 + (int64_t)m * H) * D + R * g;
+        x.kx.load(k + off);
+        x.qx.load(q + off);
+    } else {
+        x.kx.zero();
+        x.qx.zero();
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if (4 * g + s < nv) x.ku[s].load(k + (tok0 + (int64_t)(4 * g + s) * H) * D + NMT * m);
+        else x.ku[s].zero();
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        x.v[j] = (4 * g + j < nv)
+                     ? to_f32<AT>(__builtin_nontemporal_load(v + (tok0 + (int64_t)(4 * g + j) * H) * D + row))
+                     : 0.0f;
+    const float* rec = wsh + (size_t)c * REC;
+    x.tb = *(const f32x4*)(rec + REC_T + CH * m + 4 * g);
+    x.pm = *(const f32x4*)(rec + REC_P + CH * m + 4 * g);
+    x.gm = *(const f32x4*)(rec + REC_G + 4 * g);
+    x.ge = *(const f32x4*)(rec + REC_GE + 4 * g);
+    x.gend = rec[REC_G + CH - 1];
+}
+
+template <int D, typename AT>
+__device__ __forceinline__ void chunk_step(f32x4 (&S)[D / 16], const ChunkOps<D, AT>& x, int c,
+                                           int T, int H, int64_t b, int h, int row, AT* __restrict__ o,
+                                           float scale, int g) {
+    constexpr int R = D / 4, NMT = D / 16;
+    // X = K S^T and Y = Q S^T; lane (g, n) ends with rows (tokens) 4g + j of state row n.
+    f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+        const float s = S[e % NMT][e / NMT];
+        X = mfma4(x.kx.get(e), s, X);
+        Y = mfma4(x.qx.get(e), s, Y);
+    }
+    // Z = V - gamma . X, then Delta = T diag(beta) Z (step s contracts over tokens 4g + s).
+    f32x4 Z, Dl = {0.f, 0.f, 0.f, 0.f}, O;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        Z[j] = fmaf(-x.gm[j], X[j], x.v[j]);
+        O[j] = (scale * x.gm[j]) * Y[j];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Dl = mfma4(x.tb[s], Z[s], Dl);
+    // O = scale gamma . Y + P Delta.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) O = mfma4(x.pm[s], Dl[s], O);
+    // S <- gamma_15 S + K^T diag(Gam_end) Delta, tile by tile of 16 key columns.
+    f32x4 Dt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Dt[j] = x.ge[j] * Dl[j];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) S[mt] *= x.gend;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) S[mt] = mfma4(x.ku[s].get(mt), Dt[s], S[mt]);
+
+    const int t0 = c * CH;
+    const int nv = min(CH, T - t0);
+    const int64_t tok0 = (b * T + t0) * H + h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (4 * g + j < nv) o[(tok0 + (int64_t)(4 * g + j) * H) * D + row] = from_f32<AT>(O[j]);
+}
+
+// One wave per (b, h, tile of 16 state rows). With `remap`, workgroup ids are regrouped so the
+// D/16 tiles of a head run on one XCD (workgroup i runs on XCD i % 8) and share its L2 for the
+// head's k, q and chunk records.
+template <int D, typename AT, typename ST>
+__global__ __launch_bounds__(64) void gdn_prefill_state_kernel(
+    int T, int H, int nch, const AT* __restrict__ q, const AT* __restrict__ k,
+    const AT* __restrict__ v, const float* __restrict__ ws, ST* __restrict__ state,
+    AT* __restrict__ o, float scale, int remap) {
+    constexpr int R = D / 4, NMT = D / 16, NTILE = D / 16;
+    const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
+    uint32_t w = blockIdx.x;
+    if (remap) w = (w & 7u) * (gridDim.x >> 3) + (w >> 3);
+    const int nt = (int)(w % NTILE);
+    const int64_t bh = w / NTILE;
+    const int64_t b = bh / H;
+    const int h = (int)(bh % H);
+    const int row = 16 * nt + n;
+
+    ST* srow = state + ((size_t)bh * D + row) * D + R * g;
+    f32x4 S[NMT];
+    {
+        Run<ST, R> sr;
+        sr.template load<true>(srow);
+#pragma unroll
+        for (int e = 0; e < R; ++e) S[e % NMT][e / NMT] = sr.get(e);
+    }
+
+    const float* wsh = ws + (size_t)bh * nch * REC;
+    ChunkOps<D, AT> A, Bo;
+    load_chunk<D, AT>(A, 0, T, H, b, h, row, q, k, v, wsh, g, n);
+    for (int c = 0; c < nch; c += 2) {
+        if (c + 1 < nch) load_chunk<D, AT>(Bo, c + 1, T, H, b, h, row, q, k, v, wsh, g, n);
+        chunk_step<D, AT>(S, A, c, T, H, b, h, row, o, scale, g);
+        if (c + 1 >= nch) break;
+        if (c + 2 < nch) load_chunk<D, AT>(A, c + 2, T, H, b, h, row, q, k, v, wsh, g, n);
+        chunk_step<D, AT>(S, Bo, c + 1, T, H, b, h, row, o, scale, g);
+    }
+
+    float out[R];
+#pragma unroll
+    for (int e = 0; e < R; ++e) out[e] = S[e % NMT][e / NMT];
+    store_run<ST, R, true>(srow, out);
+}
+
+// ------------------------------------------------------------------------ dispatch
+
+template <int D, typename AT, typename ST>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
+    int T = a.T, H = a.H;
+    int nch = (int)prefill_chunks(a.T);
+    const AT* q = (const AT*)a.q;
+    const AT* k = (const AT*)a.k;
+    const AT* v = (const AT*)a.v;
+    const float* alpha = a.alpha;
+    const float* beta = a.beta;
+    float* ws = a.ws;
+    const float* wsc = a.ws;
+    ST* state = (ST*)a.state;
+    AT* o = (AT*)a.o;
+    float scale = a.scale;
+    const int64_t heads = a.B * a.H;
+    void* pargs[] = {&T, &H, &nch, &q, &k, &alpha, &beta, &ws, &scale};
+    hipError_t e = hipLaunchKernel((const void*)gdn_prefill_prep_kernel<D, AT>,
+                                   dim3((unsigned)(heads * nch)), dim3(64), pargs, 0, s);
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)(heads * (D / 16));
+    int remap = (grid % 8u == 0u) ? 1 : 0;
+    void* sargs[] = {&T, &H, &nch, &q, &k, &v, &wsc, &state, &o, &scale, &remap};
+    return hipLaunchKernel((const void*)gdn_prefill_state_kernel<D, AT, ST>, dim3(grid), dim3(64),
+                           sargs, 0, s);
+}
+
+template <int D, typename ST>
+hipError_t launch_prefill_s(const PrefillArgs& a, hipStream_t s) {
+    switch (a.act) {
+        case DType::F32: return launch_prefill_t<D, float, ST>(a, s);
+        case DType::BF16: return launch_prefill_t<D, uint16_t, ST>(a, s);
+        default: return launch_prefill_t<D, _Float16, ST>(a, s);
+    }
+}
+
+template <int D>
+hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t s) {
+    switch (a.state_dtype) {
+        case DType::F32: return launch_prefill_s<D, float>(a, s);
+        case DType::BF16: return launch_prefill_s<D, uint16_t>(a, s);
+        default: return launch_prefill_s<D, _Float16>(a, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    switch (a.D) {
+        case 16: return launch_prefill_d<16>(a, s);
+        case 32: return launch_prefill_d<32>(a, s);
+        case 64: return launch_prefill_d<64>(a, s);
+        default: return launch_prefill_d<128>(a, s);
+    }
+}
+
+}  // namespace gdn

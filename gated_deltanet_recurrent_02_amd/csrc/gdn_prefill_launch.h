@@ -1,0 +1,42 @@
+// Internal interface between the C-ABI layer (gdn_api.cpp) and the chunked prefill kernels
+// (gdn_prefill.hip). Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_launch.h"
+
+namespace gdn {
+
+// Tokens per chunk, and floats per chunk record in the workspace:
+//   [0, 256)   T diag(beta): T = (I + A)^-1 of the chunk, columns scaled by beta   [t][s]
+//   [256, 512) P: scale * Gam_ts * (q_t . k_s) for s <= t, 0 above the diagonal     [t][s]
+//   [512, 528) gamma_t: alpha_0 ... alpha_t (alpha = 1 past the end of the sequence)
+//   [528, 544) Gam_end,t: alpha_{t+1} ... alpha_15
+constexpr int kPrefillChunk = 16;
+constexpr int kPrefillRecordFloats = 544;
+
+struct PrefillArgs {
+    int64_t B;
+    int32_t T, H, D;          // D = dk = dv
+    const void* q;            // act [B][T][H][D]
+    const void* k;
+    const void* v;
+    DType act;
+    const float* alpha;       // [B][T][H]
+    const float* beta;
+    void* state;              // state dtype [B][H][D][D]
+    DType state_dtype;
+    void* o;                  // act [B][T][H][D]
+    float scale;
+    float* ws;                // [B][H][ceil(T/16)][kPrefillRecordFloats]
+};
+
+// Workgroups each kernel launches (both must be < 2^31; checked by the caller).
+inline int64_t prefill_chunks(int32_t T) { return (T + kPrefillChunk - 1) / kPrefillChunk; }
+
+// Enqueues the prep kernel, then the state kernel; nothing is synchronised.
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace gdn

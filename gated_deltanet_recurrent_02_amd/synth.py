@@ -10,7 +10,9 @@ Recipes (no trained weights or live activations exist for this path, so these st
       q, k   ~ N(0, 1), each (sequence, token, head) vector scaled to unit length in fp64
       v      ~ N(0, 1)
       beta   = logistic(z),                z ~ N(0, 1)
-      alpha  = exp(-softplus(z + shift)),  z ~ N(0, 1)   (shift 2 by default)
+      alpha  = exp(-softplus(z + shift)),  z ~ N(0, 1)   (shift 2 by default; -2 for the
+                                                          prompt workload, whose 4096 tokens
+                                                          keep a median alpha of 0.88)
     draw order: state, q, k, v, beta-logit, alpha-logit; one PCG64 stream per workload.
   * Fused-layer workloads take raw activations:
       qkv ~ N(0, 1) bf16 [B,T,C], conv_state ~ N(0, 1) bf16 [B,C,3], conv_w ~ N(0, 0.5) fp32 [C,4],
@@ -34,6 +36,9 @@ WORKLOADS = {
     "decode_b256_h48_d128_t1": dict(B=256, H=48, D=128, T=1, act="bf16", state_init="normal"),
     "decode_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, act="bf16", state_init="normal"),
     "fused_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, fused=True),
+    # a batch of long prompts run through the recurrence in one call (prefill)
+    "prefill_b4_h48_d128_t4096": dict(B=4, H=48, D=128, T=4096, act="bf16", state_init="normal",
+                                      alpha_shift=-2.0, prefill=True),
     # speculative verify rounds of 4 tokens; the accepted prefix per sequence is drawn by
     # accepted_prefix() below
     "verify_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, act="bf16", state_init="normal",
@@ -116,6 +121,7 @@ def workload_inputs(name: str, *, seed: int = 0, **overrides) -> dict:
     spec = dict(WORKLOADS[name])
     fused = spec.pop("fused", False)
     spec.pop("verify", False)
+    spec.pop("prefill", False)
     spec.update(overrides)
     if fused:
         return fused_inputs(seed=seed, **spec)

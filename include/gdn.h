@@ -167,6 +167,38 @@ gdn_status gdn_conv_gate_decode(int64_t B, int32_t T, int32_t H, int32_t dk, int
                                 void* state, gdn_dtype state_dtype,
                                 void* o, float scale, float l2_eps, void* stream);
 
+/*
+ * gdn_prefill_workspace_size — bytes of device workspace gdn_prefill needs for these sizes:
+ * B * H * ceil(T / 16) * 2176 (one record per head and chunk of 16 tokens); 0 when B or T is 0.
+ * Errors: GDN_ERR_INVALID_ARGUMENT (bytes NULL, bad size), GDN_ERR_UNSUPPORTED (head dims).
+ */
+gdn_status gdn_prefill_workspace_size(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                      size_t* bytes);
+
+/*
+ * gdn_prefill — the recurrent step of gdn_decode_step for a long run of T tokens (a prompt),
+ * computed in the chunked form that "GDN tuning limits on Kunlun XPU", section 三.3, uses for
+ * prefill: tokens are taken 16 at a time and the state is touched by dense products on the
+ * matrix cores instead of one rank-1 update per token. The result is that of gdn_decode_step
+ * on the same arguments up to fp32 rounding order (the state after the last token, and o for
+ * every token); both read the state once and write it once.
+ *
+ *   q, k, v, alpha, beta, state, o, scale, act_dtype, state_dtype  as gdn_decode_step
+ *   workspace        device buffer of at least gdn_prefill_workspace_size(...) bytes, owned
+ *                    by the caller; its contents on entry do not matter and on return are
+ *                    unspecified. It must not overlap any other argument. Two calls in flight
+ *                    at once need two workspaces.
+ *   workspace_bytes  its size in bytes
+ * Errors: as gdn_decode_step; GDN_ERR_INVALID_ARGUMENT also for a workspace smaller than
+ * required; GDN_ERR_UNSUPPORTED when B * H * ceil(T / 16) >= 2^31.
+ */
+gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                       const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                       const float* alpha, const float* beta,
+                       void* state, gdn_dtype state_dtype,
+                       void* o, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* gdn_status_string — static name of a status code ("GDN_OK", ...; "unknown" otherwise). */
 const char* gdn_status_string(gdn_status s);
 

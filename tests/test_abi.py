@@ -226,3 +226,59 @@ def test_decode_verify_empty_parts_may_be_null():
                                        N, N, 1.0, None) == 0
     # commit only (T = 0): new-token pointers may be NULL; passes validation, fails at launch
     assert verify(T=0, q=N, o=N, dk_out=N) == HIP
+
+
+def prefill(B=2, T=40, H=4, D=16, q=None, o=None, state=None, ws=None, ws_bytes=None, act=F32):
+    """gdn_prefill with disjoint fake buffers; the workspace is exactly the required size."""
+    L = gdn.lib()
+    q = P(0) if q is None else q
+    state = P(80 * MB) if state is None else state
+    o = P(160 * MB) if o is None else o
+    ws = P(200 * MB) if ws is None else ws
+    if ws_bytes is None:
+        try:
+            ws_bytes = gdn.prefill_workspace_size(B, T, H, D, D)
+        except gdn.GDNError:
+            ws_bytes = 1 << 30
+    return L.gdn_prefill(B, T, H, D, D, q, P(16 * MB), P(32 * MB), act, P(48 * MB), P(64 * MB),
+                         state, F32, o, 1.0, ws, ws_bytes, None)
+
+
+def test_prefill_workspace_size():
+    # one record of 544 fp32 per (b, h, chunk of 16 tokens)
+    assert gdn.prefill_workspace_size(4, 4096, 48, 128, 128) == 4 * 48 * 256 * 2176
+    assert gdn.prefill_workspace_size(2, 17, 3, 16, 16) == 2 * 3 * 2 * 2176
+    assert gdn.prefill_workspace_size(2, 16, 3, 64, 64) == 2 * 3 * 1 * 2176
+    assert gdn.prefill_workspace_size(0, 16, 3, 64, 64) == 0
+    assert gdn.prefill_workspace_size(2, 0, 3, 64, 64) == 0
+    L = gdn.lib()
+    n = ctypes.c_size_t(7)
+    assert L.gdn_prefill_workspace_size(2, 16, 3, 48, 48, ctypes.byref(n)) == UNSUPPORTED
+    assert L.gdn_prefill_workspace_size(2, 16, 3, 64, 64, None) == INVALID
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H=0), INVALID, "H must be"),
+    (dict(D=96), UNSUPPORTED, "head dims"),
+    (dict(act=9), INVALID, "dtype"),
+    (dict(ws=ctypes.c_void_p(0)), INVALID, "workspace is NULL"),
+    (dict(ws=P(200 * MB + 8)), INVALID, "workspace is not 16-byte aligned"),
+    (dict(ws_bytes=1000), INVALID, "needed"),
+    (dict(ws=P(16 * MB)), INVALID, "workspace overlaps k"),
+    (dict(o=P(200 * MB)), INVALID, "o overlaps workspace"),
+    (dict(state=P(200 * MB)), INVALID, "state overlaps workspace"),
+    (dict(B=1 << 20, H=1 << 10, T=64), UNSUPPORTED, "ceil(T / 16)"),
+])
+@fake_ptrs
+def test_prefill_rejects(kw, status, msg):
+    assert prefill(**kw) == status
+    assert msg in last_error()
+
+
+@fake_ptrs
+def test_prefill_empty_work_and_valid_call_without_device():
+    N = ctypes.c_void_p(0)
+    assert gdn.lib().gdn_prefill(0, 16, 4, 16, 16, N, N, N, F32, N, N, N, F32, N, 1.0, N, 0, None) == 0
+    assert gdn.lib().gdn_prefill(2, 0, 4, 16, 16, N, N, N, F32, N, N, N, F32, N, 1.0, N, 0, None) == 0
+    assert prefill() == HIP
+    assert "kernel launch" in last_error()

@@ -1,0 +1,148 @@
+"""gdn_prefill (the chunked form of T tokens) on the GPU against the fp64 oracle.
+
+The oracle is the plain recurrence token by token (oracle_gdn_decode); the chunked form must
+reach the same state and outputs within the floating-point bars of parity.py. Small shapes are
+compared on every head, with ragged last chunks (T not a multiple of 16) and several chunks;
+the prompt workload (B=4, H=48, D=128, T=4096) on sampled heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_recurrent_02_amd as gdn
+from gated_deltanet_recurrent_02_amd import synth
+from parity import check_o, check_state, f64, oracle_decode, sample_heads, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def gpu_prefill(x, scale=1.0, workspace=None):
+    g = to_dev(x)
+    o = gdn.prefill(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state"], scale=scale,
+                    workspace=workspace)
+    torch.cuda.synchronize()
+    return g["state"], o
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("B,H,T", [(2, 3, 1), (1, 2, 16), (3, 2, 37), (1, 3, 100)])
+def test_small_shapes_full_compare(D, act, B, H, T):
+    _announce(f"prefill B={B} H={H} D={D} T={T} act={act} state=f32")
+    x = synth.decode_inputs(B, H, D, T, act=act, alpha_shift=-2.0, state_std=0.3, seed=D + T)
+    S, o = gpu_prefill(x, scale=0.7)
+    S_ref, o_ref = oracle_decode(x, scale=0.7)
+    check_state(f64(S), S_ref, torch.float32)
+    check_o(f64(o), o_ref, DT[act])
+
+
+@pytest.mark.parametrize("sdt", ["bf16", "f16"])
+@pytest.mark.parametrize("T", [5, 48, 77])
+def test_16bit_state(sdt, T):
+    _announce(f"prefill B=2 H=4 D=128 T={T} act=bf16 state={sdt}")
+    x = synth.decode_inputs(2, 4, 128, T, act="bf16", state_dtype=sdt, alpha_shift=-2.0,
+                            state_std=0.3, seed=T)
+    S, o = gpu_prefill(x)
+    S_ref, o_ref = oracle_decode(x)
+    check_state(f64(S), S_ref, DT[sdt])
+    check_o(f64(o), o_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_prompt_workload_sampled(sdt):
+    name = "prefill_b4_h48_d128_t4096"
+    _announce(f"{name} state={sdt}")
+    x = synth.workload_inputs(name, state_dtype=sdt)
+    S0 = x["state"].clone()
+    S, o = gpu_prefill(x)
+    B, H = x["B"], x["H"]
+    heads = sample_heads(B, H, 4, seed=5)
+    S_ref, o_ref = oracle_decode(dict(x, state=S0), heads=heads)
+    Sg, og = f64(S), f64(o)
+    for n, (b, h) in enumerate(heads):
+        check_state(Sg[b, h][None], S_ref[n][None], DT[sdt], what=f"state of head ({b}, {h})")
+        check_o(og[b, :, h][None], o_ref[n][None], torch.bfloat16)
+
+
+def test_agrees_with_decode_step():
+    # The same call through the token-by-token kernel: both within the bars of the oracle, and
+    # the two fp32 states within the fp32 bar of each other.
+    _announce("prefill vs decode_step B=2 H=6 D=128 T=300")
+    x = synth.decode_inputs(2, 6, 128, 300, act="bf16", alpha_shift=-2.0, seed=11)
+    S_p, o_p = gpu_prefill(x)
+    g = to_dev(x)
+    o_d = gdn.decode_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state"])
+    torch.cuda.synchronize()
+    S_ref, o_ref = oracle_decode(x)
+    for S, o in ((S_p, o_p), (g["state"], o_d)):
+        check_state(f64(S), S_ref, torch.float32)
+        check_o(f64(o), o_ref, torch.bfloat16)
+    check_state(f64(S_p), f64(g["state"]), torch.float32)
+
+
+def test_gate_edge_values():
+    # alpha = 0 wipes the state at that token (the products of alphas carry the exact zero);
+    # beta = 0 leaves a token without a write; a zero key writes nothing.
+    _announce("prefill gate edge values")
+    x = synth.decode_inputs(2, 3, 64, 50, act="f32", alpha_shift=-2.0, state_std=0.3, seed=3)
+    x["alpha"][0, 7, :] = 0.0
+    x["alpha"][1, 16, 1] = 0.0      # first token of the second chunk
+    x["alpha"][1, 31, 2] = 0.0      # last token of the second chunk
+    x["beta"][0, 20:24, :] = 0.0
+    x["k"][1, 40, 0] = 0.0
+    x["alpha"][0, 45:, 2] = 1.0
+    S, o = gpu_prefill(x, scale=0.5)
+    S_ref, o_ref = oracle_decode(x, scale=0.5)
+    check_state(f64(S), S_ref, torch.float32)
+    check_o(f64(o), o_ref, torch.float32)
+
+
+def test_workspace_contents_do_not_matter():
+    _announce("prefill stale workspace")
+    x = synth.decode_inputs(2, 4, 32, 45, act="bf16", seed=4)
+    ws = gdn.prefill_workspace(x["q"].cuda(), x["v"].cuda())
+    ws.view(torch.float32).fill_(float("nan"))
+    S1, o1 = gpu_prefill(x, workspace=ws)
+    S2, o2 = gpu_prefill(x)
+    assert torch.equal(S1, S2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_deterministic():
+    _announce("prefill determinism")
+    x = synth.decode_inputs(4, 8, 128, 70, act="bf16", seed=6)
+    S1, o1 = gpu_prefill(x)
+    S2, o2 = gpu_prefill(x)
+    assert torch.equal(S1, S2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_empty_calls_leave_state_unchanged():
+    _announce("prefill empty calls")
+    for B, T in ((0, 5), (2, 0)):
+        x = synth.decode_inputs(max(B, 1), 2, 16, max(T, 1), act="f32", seed=7)
+        st = x["state"].cuda()[:B] if B == 0 else x["state"].cuda()
+        q = x["q"].cuda()[:B, :T].contiguous()
+        v = x["v"].cuda()[:B, :T].contiguous()
+        a = x["alpha"].cuda()[:B, :T].contiguous()
+        before = st.clone()
+        o = gdn.prefill(q, q, v, a, a.clone(), st)
+        torch.cuda.synchronize()
+        assert o.numel() == 0 and torch.equal(st, before)
+
+
+def test_split_calls_continue_the_state():
+    # Two calls of 40 and 33 tokens equal one call of 73 (the state carries everything).
+    _announce("prefill split calls")
+    x = synth.decode_inputs(2, 3, 128, 73, act="f32", alpha_shift=-2.0, seed=8)
+    g = to_dev(x)
+    o1 = gdn.prefill(*(g[n][:, :40].contiguous() for n in ("q", "k", "v", "alpha", "beta")), g["state"])
+    o2 = gdn.prefill(*(g[n][:, 40:].contiguous() for n in ("q", "k", "v", "alpha", "beta")), g["state"])
+    torch.cuda.synchronize()
+    S_ref, o_ref = oracle_decode(x)
+    check_state(f64(g["state"]), S_ref, torch.float32)
+    check_o(np.concatenate([f64(o1), f64(o2)], axis=1), o_ref, torch.float32)
