@@ -255,45 +255,49 @@ __global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
 
 // ------------------------------------------------------------------------ state kernel
 
-// One lane's operands of one chunk: lane (g, m) = (lane / 16, lane % 16).
-template <int D, typename AT>
+// One lane's operands of one chunk: lane (g, m) = (lane / 16, lane % 16). Loads never branch:
+// past the end of the sequence they read the last token again (always in bounds). Those
+// tokens then contribute exact zeros: their rows and columns of T diag(beta) are zero (beta = 0
+// in the record), so only their entries of Z are cleared, which also keeps a non-finite value
+// in the last token from reaching earlier tokens through 0 * inf. Branch-free loads let the
+// next chunk's loads stay in flight while the current chunk computes.
+template <int D, int RT, typename AT>
 struct ChunkOps {
     static constexpr int R = D / 4, NMT = D / 16;
     Run<AT, R> kx, qx;   // a operands of K S^T and Q S^T: token m, columns R g .. R g + R - 1
     Run<AT, NMT> ku[4];  // a operand of the update, step s: token 4g + s, columns NMT m .. + NMT
-    float v[4];          // v[token 4g + j][state row]
+    AT v[RT][4];         // v[token 4g + j][state row of tile r], raw
     f32x4 tb, pm;        // T diag(beta)[m][4g .. 4g+3], P[m][4g .. 4g+3]
     f32x4 gm, ge;        // gamma and Gam_end of tokens 4g .. 4g+3
     float gend;          // gamma_15: decay of the whole chunk
+    int nv;              // tokens of the chunk inside the sequence (1..16)
 };
 
-template <int D, typename AT>
-__device__ __forceinline__ void load_chunk(ChunkOps<D, AT>& x, int c, int T, int H, int64_t b,
-                                           int h, int row, const AT* __restrict__ q,
+template <int D, int RT, typename AT>
+__device__ __forceinline__ void load_chunk(ChunkOps<D, RT, AT>& x, int c, int T, int H, int64_t b,
+                                           int h, int row0, const AT* __restrict__ q,
                                            const AT* __restrict__ k, const AT* __restrict__ v,
                                            const float* __restrict__ wsh, int g, int m) {
     constexpr int R = D / 4, NMT = D / 16;
     const int t0 = c * CH;
     const int nv = min(CH, T - t0);
+    x.nv = nv;
     const int64_t tok0 = (b * T + t0) * H + h;  // index of (b, t0, h) in [B][T][H]
-    if (m < nv) {
-        const int64_t off = (tok0 + (int64_t)m * H) * D + R * g;
+    const int last = nv - 1;
+    {
+        const int64_t off = (tok0 + (int64_t)min(m, last) * H) * D + R * g;
         x.kx.load(k + off);
         x.qx.load(q + off);
-    } else {
-        x.kx.zero();
-        x.qx.zero();
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        if (4 * g + s < nv) x.ku[s].load(k + (tok0 + (int64_t)(4 * g + s) * H) * D + NMT * m);
-        else x.ku[s].zero();
-    }
+    for (int s = 0; s < 4; ++s)
+        x.ku[s].load(k + (tok0 + (int64_t)min(4 * g + s, last) * H) * D + NMT * m);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        x.v[j] = (4 * g + j < nv)
-                     ? to_f32<AT>(__builtin_nontemporal_load(v + (tok0 + (int64_t)(4 * g + j) * H) * D + row))
-                     : 0.0f;
+    for (int j = 0; j < 4; ++j) {
+        const AT* vt = v + (tok0 + (int64_t)min(4 * g + j, last) * H) * D + row0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) x.v[r][j] = __builtin_nontemporal_load(vt + 16 * r);
+    }
     const float* rec = wsh + (size_t)c * REC;
     x.tb = *(const f32x4*)(rec + REC_T + CH * m + 4 * g);
     x.pm = *(const f32x4*)(rec + REC_P + CH * m + 4 * g);
@@ -302,92 +306,150 @@ __device__ __forceinline__ void load_chunk(ChunkOps<D, AT>& x, int c, int T, int
     x.gend = rec[REC_G + CH - 1];
 }
 
-template <int D, typename AT>
-__device__ __forceinline__ void chunk_step(f32x4 (&S)[D / 16], const ChunkOps<D, AT>& x, int c,
-                                           int T, int H, int64_t b, int h, int row, AT* __restrict__ o,
+// One chunk for the wave's RT tiles of 16 state rows; tile r holds rows row0 + 16 r (lane's
+// row n of the tile). Tiles are interleaved innermost so that consecutive products are
+// independent. The registers hold S' = S / c with c a wave-uniform running product of the
+// chunk decays, so the decay of the state costs per-token factors instead of a multiply per
+// state element: X = c K S'^T, and S_end = gamma_15 c (S' + K^T diag(Gam_end) Delta / (gamma_15 c)).
+// When gamma_15 c leaves [2^-64, 2^64] (alpha = 0, long strong decay, or alpha > 1 or < 0) the
+// product is folded into S' first and c restarts at 1.
+template <int D, int RT, typename AT>
+__device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
+                                           const ChunkOps<D, RT, AT>& x, int ci, int T, int H,
+                                           int64_t b, int h, int row0, AT* __restrict__ o,
                                            float scale, int g) {
     constexpr int R = D / 4, NMT = D / 16;
-    // X = K S^T and Y = Q S^T; lane (g, n) ends with rows (tokens) 4g + j of state row n.
-    f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+    const int nv = x.nv;
+    // X' = K S'^T and Y' = Q S'^T; lane (g, n) ends with rows (tokens) 4g + j of state row n.
+    f32x4 X[RT], Y[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) X[r] = Y[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < R; ++e) {
-        const float s = S[e % NMT][e / NMT];
-        X = mfma4(x.kx.get(e), s, X);
-        Y = mfma4(x.qx.get(e), s, Y);
+        const float ke = x.kx.get(e), qe = x.qx.get(e);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const float s = S[r][e % NMT][e / NMT];
+            X[r] = mfma4(ke, s, X[r]);
+            Y[r] = mfma4(qe, s, Y[r]);
+        }
     }
-    // Z = V - gamma . X, then Delta = T diag(beta) Z (step s contracts over tokens 4g + s).
-    f32x4 Z, Dl = {0.f, 0.f, 0.f, 0.f}, O;
+    // Z = V - gamma c . X', then Delta = T diag(beta) Z (step s contracts over tokens 4g + s).
+    f32x4 gx, gy;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        Z[j] = fmaf(-x.gm[j], X[j], x.v[j]);
-        O[j] = (scale * x.gm[j]) * Y[j];
+        gx[j] = x.gm[j] * c;
+        gy[j] = gx[j] * scale;
     }
+    f32x4 Z[RT], Dl[RT], O[RT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) Dl = mfma4(x.tb[s], Z[s], Dl);
-    // O = scale gamma . Y + P Delta.
+    for (int r = 0; r < RT; ++r) {
+        Dl[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) O = mfma4(x.pm[s], Dl[s], O);
-    // S <- gamma_15 S + K^T diag(Gam_end) Delta, tile by tile of 16 key columns.
-    f32x4 Dt;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Dt[j] = x.ge[j] * Dl[j];
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) S[mt] *= x.gend;
+        for (int j = 0; j < 4; ++j) {
+            Z[r][j] = (4 * g + j < nv) ? fmaf(-gx[j], X[r][j], to_f32<AT>(x.v[r][j])) : 0.0f;
+            O[r][j] = gy[j] * Y[r][j];
+        }
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) S[mt] = mfma4(x.ku[s].get(mt), Dt[s], S[mt]);
+        for (int r = 0; r < RT; ++r) Dl[r] = mfma4(x.tb[s], Z[r][s], Dl[r]);
+    // O = scale gamma c . Y' + P Delta.
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) O[r] = mfma4(x.pm[s], Dl[r][s], O[r]);
+    // S' <- S' + K^T diag(Gam_end / c_new) Delta with c_new = gamma_15 c, tile by tile of 16 key
+    // columns (after folding c_new into S' when it is out of range).
+    float cn = x.gend * c;
+    if (!(fabsf(cn) >= 0x1p-64f && fabsf(cn) <= 0x1p64f)) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) S[r][mt] *= cn;
+        cn = 1.0f;
+    }
+    c = cn;
+    const float rc = 1.0f / cn;
+    f32x4 Dt[RT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float f = x.ge[j] * rc;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) Dt[r][j] = f * Dl[r][j];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+            const float ks = x.ku[s].get(mt);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) S[r][mt] = mfma4(ks, Dt[r][s], S[r][mt]);
+        }
 
-    const int t0 = c * CH;
-    const int nv = min(CH, T - t0);
-    const int64_t tok0 = (b * T + t0) * H + h;
+    const int64_t tok0 = (b * T + ci * CH) * H + h;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        if (4 * g + j < nv) o[(tok0 + (int64_t)(4 * g + j) * H) * D + row] = from_f32<AT>(O[j]);
+        if (4 * g + j < nv) {
+            AT* ot = o + (tok0 + (int64_t)(4 * g + j) * H) * D + row0;
+#pragma unroll
+            for (int r = 0; r < RT; ++r) ot[16 * r] = from_f32<AT>(O[r][j]);
+        }
 }
 
-// One wave per (b, h, tile of 16 state rows). With `remap`, workgroup ids are regrouped so the
-// D/16 tiles of a head run on one XCD (workgroup i runs on XCD i % 8) and share its L2 for the
+// One wave per (b, h, RT tiles of 16 state rows). With `remap`, workgroup ids are regrouped so
+// the waves of a head run on one XCD (workgroup i runs on XCD i % 8) and share its L2 for the
 // head's k, q and chunk records.
-template <int D, typename AT, typename ST>
+template <int D, int RT, typename AT, typename ST>
 __global__ __launch_bounds__(64) void gdn_prefill_state_kernel(
     int T, int H, int nch, const AT* __restrict__ q, const AT* __restrict__ k,
     const AT* __restrict__ v, const float* __restrict__ ws, ST* __restrict__ state,
     AT* __restrict__ o, float scale, int remap) {
-    constexpr int R = D / 4, NMT = D / 16, NTILE = D / 16;
+    constexpr int R = D / 4, NMT = D / 16, NW = D / (16 * RT);
+    static_assert(NW * 16 * RT == D, "tiles per wave");
     const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
     uint32_t w = blockIdx.x;
     if (remap) w = (w & 7u) * (gridDim.x >> 3) + (w >> 3);
-    const int nt = (int)(w % NTILE);
-    const int64_t bh = w / NTILE;
+    const int wt = (int)(w % NW);
+    const int64_t bh = w / NW;
     const int64_t b = bh / H;
     const int h = (int)(bh % H);
-    const int row = 16 * nt + n;
+    const int row0 = 16 * RT * wt + n;
 
-    ST* srow = state + ((size_t)bh * D + row) * D + R * g;
-    f32x4 S[NMT];
-    {
-        Run<ST, R> sr;
-        sr.template load<true>(srow);
+    f32x4 S[RT][NMT];
 #pragma unroll
-        for (int e = 0; e < R; ++e) S[e % NMT][e / NMT] = sr.get(e);
+    for (int r = 0; r < RT; ++r) {
+        Run<ST, R> sr;
+        sr.template load<true>(state + ((size_t)bh * D + row0 + 16 * r) * D + R * g);
+#pragma unroll
+        for (int e = 0; e < R; ++e) S[r][e % NMT][e / NMT] = sr.get(e);
     }
 
     const float* wsh = ws + (size_t)bh * nch * REC;
-    ChunkOps<D, AT> A, Bo;
-    load_chunk<D, AT>(A, 0, T, H, b, h, row, q, k, v, wsh, g, n);
+    float cs = 1.0f;  // S = cs S' (wave-uniform)
+    ChunkOps<D, RT, AT> A, Bo;
+    load_chunk<D, RT, AT>(A, 0, T, H, b, h, row0, q, k, v, wsh, g, n);
+    // The prefetches are unconditional (the last chunk is read again at the end): a load that
+    // only some paths issue would make the compiler wait for every load in flight. The
+    // scheduling barriers keep them ahead of the chunk's products instead of sunk to its end.
     for (int c = 0; c < nch; c += 2) {
-        if (c + 1 < nch) load_chunk<D, AT>(Bo, c + 1, T, H, b, h, row, q, k, v, wsh, g, n);
-        chunk_step<D, AT>(S, A, c, T, H, b, h, row, o, scale, g);
+        load_chunk<D, RT, AT>(Bo, min(c + 1, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+        __builtin_amdgcn_sched_barrier(0);
+        chunk_step<D, RT, AT>(S, cs, A, c, T, H, b, h, row0, o, scale, g);
         if (c + 1 >= nch) break;
-        if (c + 2 < nch) load_chunk<D, AT>(A, c + 2, T, H, b, h, row, q, k, v, wsh, g, n);
-        chunk_step<D, AT>(S, Bo, c + 1, T, H, b, h, row, o, scale, g);
+        load_chunk<D, RT, AT>(A, min(c + 2, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+        __builtin_amdgcn_sched_barrier(0);
+        chunk_step<D, RT, AT>(S, cs, Bo, c + 1, T, H, b, h, row0, o, scale, g);
     }
 
-    float out[R];
 #pragma unroll
-    for (int e = 0; e < R; ++e) out[e] = S[e % NMT][e / NMT];
-    store_run<ST, R, true>(srow, out);
+    for (int r = 0; r < RT; ++r) {
+        float out[R];
+#pragma unroll
+        for (int e = 0; e < R; ++e) out[e] = S[r][e % NMT][e / NMT] * cs;
+        store_run<ST, R, true>(state + ((size_t)bh * D + row0 + 16 * r) * D + R * g, out);
+    }
 }
 
 // ------------------------------------------------------------------------ dispatch
@@ -411,11 +473,12 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
     hipError_t e = hipLaunchKernel((const void*)gdn_prefill_prep_kernel<D, AT>,
                                    dim3((unsigned)(heads * nch)), dim3(64), pargs, 0, s);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)(heads * (D / 16));
+    constexpr int RT = (D >= 32) ? 2 : 1;  // 16-row tiles per wave
+    const unsigned grid = (unsigned)(heads * (D / (16 * RT)));
     int remap = (grid % 8u == 0u) ? 1 : 0;
     void* sargs[] = {&T, &H, &nch, &q, &k, &v, &wsc, &state, &o, &scale, &remap};
-    return hipLaunchKernel((const void*)gdn_prefill_state_kernel<D, AT, ST>, dim3(grid), dim3(64),
-                           sargs, 0, s);
+    return hipLaunchKernel((const void*)gdn_prefill_state_kernel<D, RT, AT, ST>, dim3(grid),
+                           dim3(64), sargs, 0, s);
 }
 
 template <int D, typename ST>

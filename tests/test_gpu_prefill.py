@@ -146,3 +146,20 @@ def test_split_calls_continue_the_state():
     S_ref, o_ref = oracle_decode(x)
     check_state(f64(g["state"]), S_ref, torch.float32)
     check_o(np.concatenate([f64(o1), f64(o2)], axis=1), o_ref, torch.float32)
+
+
+def test_decay_fold_paths():
+    # The kernel keeps S / c in registers with c the running product of chunk decays and folds
+    # c into the state when it leaves [2^-64, 2^64]: alpha > 1 (c grows past 2^64 within a few
+    # chunks), alpha < 0 (c changes sign: folded every chunk), tiny alphas (c underflows), and
+    # exact zeros mid-chunk, each on its own head.
+    _announce("prefill decay fold paths")
+    x = synth.decode_inputs(1, 4, 128, 100, act="f32", state_std=0.3, seed=9)
+    x["alpha"][0, :, 0] = 1.7
+    x["alpha"][0, :, 1] = -0.9
+    x["alpha"][0, :, 2] = 1e-3
+    x["alpha"][0, 5::16, 3] = 0.0
+    S, o = gpu_prefill(x, scale=0.25)
+    S_ref, o_ref = oracle_decode(x, scale=0.25)
+    check_state(f64(S), S_ref, torch.float32)
+    check_o(f64(o), o_ref, torch.float32)
