@@ -3,7 +3,10 @@
     python -m gated_deltanet_recurrent_02_amd.build        # or __graft_entry__.build()
 
 The library is the hand-written HIP kernels plus the C-ABI layer; it links only the HIP
-runtime. Packed-fp32 instruction selection is switched off (-packed-fp32-ops).
+runtime. Packed-fp32 instruction selection is switched off (-packed-fp32-ops), and matrix-core
+results are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form) so that the vector code of the
+prefill kernel reads them without accumulator-register copies; kernels without matrix-core
+instructions compile to the same code either way.
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ ARCH = "gfx950"
 HIPFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

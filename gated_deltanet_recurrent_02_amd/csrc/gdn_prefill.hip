@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn_prefill_launch.h"
 
 namespace gdn {
@@ -56,6 +58,42 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// D += A B with bf16 operands and fp32 accumulation: 16 x 16 x 32 (a, b: 8 bf16 per lane,
+// lane l holding k = 8 (l/16) .. + 7) and 16 x 16 x 16 (4 bf16 per lane, k = 4 (l/16) .. + 3);
+// the accumulator layout is that of mfma4 (checked on the device against a CPU product).
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+}
+
+// Two floats as three packed pairs of bf16 (first value in the low half) whose sum is exact:
+// x = hi + mid + lo with hi the top 8 significant bits of x (truncation), mid the top 8 of the
+// exact remainder x - hi, and lo the rest, which has at most 8 significant bits left. A
+// product with a bf16 operand is then an fp32-exact product split over three bf16 products
+// (an fp32 value carries 24 significant bits). Non-finite values stay non-finite.
+struct Split3 { uint32_t h, m, l; };
+__device__ __forceinline__ Split3 split3(float a, float b) {
+    constexpr uint32_t HI = 0xffff0000u;
+    const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    const float ra = a - __uint_as_float(ua & HI), rb = b - __uint_as_float(ub & HI);
+    const uint32_t va = __float_as_uint(ra), vb = __float_as_uint(rb);
+    const float sa = ra - __uint_as_float(va & HI), sb = rb - __uint_as_float(vb & HI);
+    return Split3{(ua >> 16) | (ub & HI), (va >> 16) | (vb & HI),
+                  (__float_as_uint(sa) >> 16) | (__float_as_uint(sb) & HI)};
+}
+
+// bf16 activations of head dim >= 32 take the bf16 matrix-core path (k and q are exact bf16
+// operands); other types and D = 16 take fp32 MFMA (16 x 16 x 4).
+template <int D, typename AT>
+constexpr bool kBf16Mma = std::is_same<AT, uint16_t>::value && D >= 32;
 
 __device__ __forceinline__ float lane_value(float x, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
@@ -204,11 +242,22 @@ __global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
 
     // G[t][s] = k_t . k_s and QK[t][s] = q_t . k_s; lane (g, n) holds rows t = 4g + j, column s = n.
     f32x4 G = {0.f, 0.f, 0.f, 0.f}, QK = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kBf16Mma<D, AT>) {
+        // 8 key columns per lane and step: words 4s .. 4s+3 of the lane's run.
 #pragma unroll
-    for (int e = 0; e < R; ++e) {
-        const float ke = kx.get(e);
-        G = mfma4(ke, ke, G);
-        QK = mfma4(qx.get(e), ke, QK);
+        for (int s = 0; s < D / 32; ++s) {
+            const u32x4 ka = {kx.w[4 * s], kx.w[4 * s + 1], kx.w[4 * s + 2], kx.w[4 * s + 3]};
+            const u32x4 qa = {qx.w[4 * s], qx.w[4 * s + 1], qx.w[4 * s + 2], qx.w[4 * s + 3]};
+            G = mfma_k32(ka, ka, G);
+            QK = mfma_k32(qa, ka, QK);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            const float ke = kx.get(e);
+            G = mfma4(ke, ke, G);
+            QK = mfma4(qx.get(e), ke, QK);
+        }
     }
 
     // Gam_ts for t = 4g + j, s = n: the product of alpha_r over s < r <= t (1 if empty), in
@@ -324,14 +373,43 @@ __device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
     f32x4 X[RT], Y[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) X[r] = Y[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kBf16Mma<D, AT>) {
+        // Step s contracts over the lane's columns t = 8s .. 8s+7 of its run (state elements
+        // (mt, i) = (t % NMT, t / NMT)); S' enters as three bf16 parts for X (which feeds the
+        // state) and two for Y (o is rounded to the activation type; the dropped part is below
+        // 2^-16 of each element).
 #pragma unroll
-    for (int e = 0; e < R; ++e) {
-        const float ke = x.kx.get(e), qe = x.qx.get(e);
+        for (int s = 0; s < D / 32; ++s) {
+            const u32x4 ka = {x.kx.w[4 * s], x.kx.w[4 * s + 1], x.kx.w[4 * s + 2], x.kx.w[4 * s + 3]};
+            const u32x4 qa = {x.qx.w[4 * s], x.qx.w[4 * s + 1], x.qx.w[4 * s + 2], x.qx.w[4 * s + 3]};
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            const float s = S[r][e % NMT][e / NMT];
-            X[r] = mfma4(ke, s, X[r]);
-            Y[r] = mfma4(qe, s, Y[r]);
+            for (int r = 0; r < RT; ++r) {
+                Split3 p[4];
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int t = 8 * s + 2 * pp;
+                    p[pp] = split3(S[r][t % NMT][t / NMT], S[r][t % NMT + 1][t / NMT]);
+                }
+                const u32x4 bh = {p[0].h, p[1].h, p[2].h, p[3].h};
+                const u32x4 bm = {p[0].m, p[1].m, p[2].m, p[3].m};
+                const u32x4 bl = {p[0].l, p[1].l, p[2].l, p[3].l};
+                X[r] = mfma_k32(ka, bh, X[r]);
+                Y[r] = mfma_k32(qa, bh, Y[r]);
+                X[r] = mfma_k32(ka, bm, X[r]);
+                Y[r] = mfma_k32(qa, bm, Y[r]);
+                X[r] = mfma_k32(ka, bl, X[r]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            const float ke = x.kx.get(e), qe = x.qx.get(e);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const float s = S[r][e % NMT][e / NMT];
+                X[r] = mfma4(ke, s, X[r]);
+                Y[r] = mfma4(qe, s, Y[r]);
+            }
         }
     }
     // Z = V - gamma c . X', then Delta = T diag(beta) Z (step s contracts over tokens 4g + s).
@@ -379,14 +457,40 @@ __device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
 #pragma unroll
         for (int r = 0; r < RT; ++r) Dt[r][j] = f * Dl[r][j];
     }
+    if constexpr (kBf16Mma<D, AT>) {
+        // 16 x 16 x 16 over the chunk's tokens 4g .. 4g+3 (lane group g): K^T as packed pairs of
+        // tokens (4g, 4g+1), (4g+2, 4g+3) of column NMT m + mt; Delta' as three bf16 parts.
+        u32x2 dh[RT], dm[RT], dl[RT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+        for (int r = 0; r < RT; ++r) {
+            const Split3 p0 = split3(Dt[r][0], Dt[r][1]), p1 = split3(Dt[r][2], Dt[r][3]);
+            dh[r] = u32x2{p0.h, p1.h};
+            dm[r] = u32x2{p0.m, p1.m};
+            dl[r] = u32x2{p0.l, p1.l};
+        }
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
-            const float ks = x.ku[s].get(mt);
+            const int wi = mt >> 1;
+            const uint32_t k0 = x.ku[0].w[wi], k1 = x.ku[1].w[wi], k2 = x.ku[2].w[wi], k3 = x.ku[3].w[wi];
+            const u32x2 ka = (mt & 1) ? u32x2{(k0 >> 16) | (k1 & 0xffff0000u), (k2 >> 16) | (k3 & 0xffff0000u)}
+                                      : u32x2{(k0 & 0xffffu) | (k1 << 16), (k2 & 0xffffu) | (k3 << 16)};
 #pragma unroll
-            for (int r = 0; r < RT; ++r) S[r][mt] = mfma4(ks, Dt[r][s], S[r][mt]);
+            for (int r = 0; r < RT; ++r) {
+                S[r][mt] = mfma_k16(ka, dh[r], S[r][mt]);
+                S[r][mt] = mfma_k16(ka, dm[r], S[r][mt]);
+                S[r][mt] = mfma_k16(ka, dl[r], S[r][mt]);
+            }
         }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+                const float ks = x.ku[s].get(mt);
+#pragma unroll
+                for (int r = 0; r < RT; ++r) S[r][mt] = mfma4(ks, Dt[r][s], S[r][mt]);
+            }
+    }
 
     const int64_t tok0 = (b * T + ci * CH) * H + h;
 #pragma unroll
