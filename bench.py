@@ -4,7 +4,10 @@
 
 A step is one layer's call of the hot path over one batch of seeded synthetic input that is
 already resident in HBM: gdn_decode_step for the decode workloads (state read once, T tokens,
-state written once), gdn_conv_gate_decode for the fused one. Layer buffers (state, inputs,
+state written once), gdn_conv_gate_decode for the fused one, gdn_decode_verify for the verify
+rounds, and gdn_prefill for the prompt workload (`--sequential` runs that workload through
+gdn_decode_step instead; its roofline prices the recurrence's flop against the fp32 matrix
+peak, as the chunked form is bound by arithmetic, not HBM). Layer buffers (state, inputs,
 outputs) are rotated so that the state a step reads was not left in the 256 MB MALL by the
 previous step. W untimed steps, then K timed steps between two device synchronisations; the
 HIP events that time them are recorded on the stream the kernels are launched on.
@@ -39,13 +42,15 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_FP32_MFMA_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "gated_deltanet_recurrent_02_amd", "csrc", f)
-                  for f in ("gdn_kernels.hip", "gdn_launch.h")]
+_CSRC = os.path.join(ROOT, "gated_deltanet_recurrent_02_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_kernels.hip", "gdn_launch.h")]
+PREFILL_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_prefill.hip", "gdn_prefill_launch.h")]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(prefill: bool = False) -> str:
+    """Hash of the kernel sources a workload runs (decode kernels or the prefill kernels)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (PREFILL_SOURCES if prefill else KERNEL_SOURCES):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -100,7 +105,7 @@ def flops(spec: dict) -> int:
     return B * H * T * (6 * D * D + 6 * D)
 
 
-def read_traffic(workload: str, state_dtype: str):
+def read_traffic(workload: str, state_dtype: str, prefill: bool = False):
     """Measured HBM bytes per launch from profiles/traffic_<workload>_<state>.txt, if the
     kernel source still hashes to the value recorded there; else None."""
     path = os.path.join(PROFILES, f"traffic_{workload}_{state_dtype}.txt")
@@ -112,7 +117,7 @@ def read_traffic(workload: str, state_dtype: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(prefill):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -317,6 +322,7 @@ def main(argv=None):
 
     from gated_deltanet_recurrent_02_amd import synth
     spec = dict(synth.WORKLOADS[args.workload])
+    chunked = bool(spec.get("prefill")) and not args.sequential
     ms, L, extra = time_gpu(args, spec, args.workload)
     us = ms * 1e3
     nbytes = algorithmic_bytes(spec, args.state_dtype)
@@ -339,21 +345,23 @@ def main(argv=None):
         "seq_tokens_per_s": B * T / (ms * 1e-3),
         "us_per_token_48_layers": us * 48,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": gbps / PEAK_HBM_GBPS, "traffic": read_traffic(args.workload, args.state_dtype),
+                     "frac": gbps / PEAK_HBM_GBPS,
+                     "traffic": read_traffic(args.workload, args.state_dtype, chunked),
                      "algorithmic_bytes_per_launch": nbytes,
-                     "kernel_source_sha256_16": kernel_source_hash()},
+                     "kernel_source_sha256_16": kernel_source_hash(chunked)},
         "gflops": flops(spec) / (ms * 1e-3) / 1e9,
     }
     line.update(extra)
     line["frac_of_copy_bw"] = gbps / extra["copy_gbps_same_bytes"]
-    if spec.get("prefill") and not args.sequential:
+    if chunked:
         # The chunked form is bound by fp32 matrix-core arithmetic, not by HBM: price the
         # recurrence's flops (per token and head: S k, S q and the rank-1 update, 6 D^2) against
         # the fp32 MFMA peak. The time is the whole call (prep kernel + state kernel).
         tf = flops(spec) / (ms * 1e-3) / 1e12
         line["roofline_hbm"] = line["roofline"]
         line["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS,
-                            "unit": "TFLOP/s", "frac": tf / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                            "unit": "TFLOP/s", "frac": tf / PEAK_FP32_MFMA_TFLOPS,
+                            "traffic": line["roofline_hbm"]["traffic"],
                             "algorithmic_flops_per_launch": flops(spec),
                             "timed": "whole gdn_prefill call (prep + state kernels)"}
     if not args.no_cpu_baseline:
