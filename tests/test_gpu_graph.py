@@ -67,3 +67,27 @@ def test_conv_gate_decode_graph_replays_match_eager():
         assert torch.equal(o.view(torch.int16), ref_o[i].view(torch.int16)), f"o of replay {i}"
         _ = cs.float().sum()
     assert torch.equal(S, ref_S) and torch.equal(cs.view(torch.int16), ref_cs.view(torch.int16))
+
+
+def test_prefill_graph_replays_match_eager():
+    # Both prefill kernels in one captured graph with a workspace allocated beforehand.
+    _announce("graph prefill B=2 H=8 D=128 T=100")
+    x = to_dev(synth.decode_inputs(2, 8, 128, 100, alpha_shift=-2.0, seed=34))
+    S0 = x["state"].clone()
+    ws = gdn.prefill_workspace(x["q"], x["v"])
+    ref_S, ref_o = S0.clone(), []
+    for _ in range(3):
+        ref_o.append(gdn.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], ref_S, workspace=ws).clone())
+    torch.cuda.synchronize()
+    S = S0.clone()
+    o = torch.empty_like(x["v"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gdn.prefill(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S, o=o, workspace=ws)
+    S.copy_(S0)
+    for i in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref_o[i].view(torch.int16)), f"o of replay {i}"
+        _ = S.float().abs().max()  # eager work between replays
+    assert torch.equal(S, ref_S)

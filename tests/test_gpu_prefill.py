@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import gated_deltanet_recurrent_02_amd as gdn
+import oracle
 from gated_deltanet_recurrent_02_amd import synth
 from parity import check_o, check_state, f64, oracle_decode, sample_heads, to_dev
 
@@ -163,3 +164,38 @@ def test_decay_fold_paths():
     S_ref, o_ref = oracle_decode(x, scale=0.25)
     check_state(f64(S), S_ref, torch.float32)
     check_o(f64(o), o_ref, torch.float32)
+
+
+def test_offsets_beyond_2_31_elements():
+    # B=16 x T=32768 x H=48 x D=128 = 3.2e9 elements per activation tensor (6.4 GB of bf16 each),
+    # so token offsets pass 2^31; 2048 chunks per head. Drawn on the device from a seeded
+    # generator; sampled heads (including the last sequence's last head) are read back and
+    # compared with the oracle over all 32768 tokens.
+    B, T, H, D = 16, 32768, 48, 128
+    _announce(f"prefill B={B} T={T} H={H} D={D} (3.2e9-element activations)")
+    gen = torch.Generator(device="cuda").manual_seed(41)
+
+    def unit(shape):
+        x = torch.randn(shape, device="cuda", generator=gen)
+        x /= x.norm(dim=-1, keepdim=True)
+        return x.bfloat16()
+
+    q, k = unit((B, T, H, D)), unit((B, T, H, D))
+    v = torch.randn((B, T, H, D), device="cuda", generator=gen).bfloat16()
+    alpha = torch.rand((B, T, H), device="cuda", generator=gen).mul_(0.3).add_(0.7)
+    beta = torch.rand((B, T, H), device="cuda", generator=gen)
+    state = torch.randn((B, H, D, D), device="cuda", generator=gen).mul_(0.3)
+    heads = [(0, 0), (B // 2, 7), (B - 1, H - 1)]
+    bi, hi = (torch.as_tensor(a) for a in np.asarray(heads).T)
+    sel = lambda t: f64(t[bi.cuda(), :, hi.cuda()])          # [n, T, ...]
+    qs, ks, vs, als, bes = (sel(t) for t in (q, k, v, alpha, beta))
+    S0 = f64(state[bi.cuda(), hi.cuda()])
+    o = gdn.prefill(q, k, v, alpha, beta, state)
+    torch.cuda.synchronize()
+    S1, o_s = f64(state[bi.cuda(), hi.cuda()]), sel(o)
+    del q, k, v, o
+    S_ref, o_ref = oracle.gdn_decode(qs[:, :, None], ks[:, :, None], vs[:, :, None],
+                                     als[:, :, None], bes[:, :, None], S0[:, None])
+    for n, (b, h) in enumerate(heads):
+        check_state(S1[n][None], S_ref[n], torch.float32, what=f"state of head ({b}, {h})")
+        check_o(o_s[n][None], o_ref[n, :, 0][None], torch.bfloat16)
