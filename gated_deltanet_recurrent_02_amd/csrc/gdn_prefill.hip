@@ -204,15 +204,19 @@ __device__ __forceinline__ void store_run(T* p, const float* x) {
 // ------------------------------------------------------------------------ prep kernel
 
 // One wave per (b, h, chunk c); workgroup id = (b H + h) nch + c, which is also the record's
-// index in the workspace. Lane (g, n) = (lane / 16, lane % 16) holds token n's q and k over the
-// columns (D/4) g .. (D/4) g + D/4 - 1, so that the same registers are the a and b operands of
-// the Gram products (the contraction runs over the key dim in any order).
+// index in the workspace. Lane (g, n) = (lane / 16, lane % 16) holds token n's k (and q) over
+// the columns (D/4) g .. (D/4) g + D/4 - 1, so that the same registers are the a and b operands
+// of the Gram products (the contraction runs over the key dim in any order).
+// With bf16 activations the record's P slot holds scale Gam_ts (s <= t, 0 above) and the state
+// kernel multiplies it by q_t . k_s, which it forms from registers it holds anyway, so this
+// kernel never reads q; for other activation types it stores P itself.
 template <int D, typename AT>
 __global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
     int T, int H, int nch, const AT* __restrict__ q, const AT* __restrict__ k,
     const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ ws,
     float scale) {
     constexpr int R = D / 4;
+    constexpr bool kFormsP = !kBf16Mma<D, AT>;
     __shared__ float sA[CH][CH];
     const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
     const uint32_t wid = blockIdx.x;
@@ -227,10 +231,10 @@ __global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
     if (n < nv) {
         const int64_t off = ((b * T + t0 + n) * H + h) * D + R * g;
         kx.load(k + off);
-        qx.load(q + off);
+        if constexpr (kFormsP) qx.load(q + off);
     } else {
         kx.zero();
-        qx.zero();
+        if constexpr (kFormsP) qx.zero();
     }
     // Lane t < 16 holds token t's gates; past the end alpha = 1, beta = 0.
     float al = 1.0f, be = 0.0f;
@@ -240,16 +244,15 @@ __global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
         be = beta[ti];
     }
 
-    // G[t][s] = k_t . k_s and QK[t][s] = q_t . k_s; lane (g, n) holds rows t = 4g + j, column s = n.
+    // G[t][s] = k_t . k_s (and QK[t][s] = q_t . k_s); lane (g, n) holds rows t = 4g + j, column
+    // s = n.
     f32x4 G = {0.f, 0.f, 0.f, 0.f}, QK = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kBf16Mma<D, AT>) {
         // 8 key columns per lane and step: words 4s .. 4s+3 of the lane's run.
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) {
             const u32x4 ka = {kx.w[4 * s], kx.w[4 * s + 1], kx.w[4 * s + 2], kx.w[4 * s + 3]};
-            const u32x4 qa = {qx.w[4 * s], qx.w[4 * s + 1], qx.w[4 * s + 2], qx.w[4 * s + 3]};
             G = mfma_k32(ka, ka, G);
-            QK = mfma_k32(qa, ka, QK);
         }
     } else {
 #pragma unroll
@@ -260,18 +263,17 @@ __global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
         }
     }
 
-    // Gam_ts for t = 4g + j, s = n: the product of alpha_r over s < r <= t (1 if empty), in
-    // increasing r; gamma_l = alpha_0 ... alpha_l and Gam_end,l = alpha_{l+1} ... alpha_15 for
-    // the lane's own token l = lane (lanes < 16).
+    // Decays of column s = n: a running product over t, Gam_{t,n} = alpha_{n+1} ... alpha_t for
+    // t > n (1 for t <= n), multiplied in increasing t; the lane keeps rows t = 4g + j. After
+    // the last token it holds Gam_end,n = Gam_{15,n}, and on the lanes of column 0,
+    // gamma_t = alpha_0 Gam_{t,0}.
+    float run = 1.0f;
     float gam[4] = {1.f, 1.f, 1.f, 1.f};
-    float gl = 1.0f, ge = 1.0f;
 #pragma unroll
-    for (int r = 0; r < CH; ++r) {
-        const float ar = lane_value(al, r);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (r > n && r <= 4 * g + j) gam[j] *= ar;
-        if (r <= lane) gl *= ar; else ge *= ar;
+    for (int t = 0; t < CH; ++t) {
+        const float at = lane_value(al, t);
+        run = (t > n) ? run * at : 1.0f;
+        if (g == t / 4) gam[t % 4] = run;
     }
 
     float* rec = ws + (size_t)wid * REC;
@@ -280,8 +282,15 @@ __global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
         const int t = 4 * g + j;
         const float bt = __shfl(be, t);
         sA[t][n] = (n < t) ? bt * gam[j] * G[j] : 0.0f;
-        rec[REC_P + t * CH + n] = (n <= t) ? scale * gam[j] * QK[j] : 0.0f;
+        const float p = kFormsP ? scale * gam[j] * QK[j] : scale * gam[j];
+        rec[REC_P + t * CH + n] = (n <= t) ? p : 0.0f;
     }
+    const float a0 = lane_value(al, 0);
+    if (n == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rec[REC_G + 4 * g + j] = a0 * gam[j];
+    }
+    if (g == 0) rec[REC_GE + n] = run;
     __syncthreads();
 
     // T = (I + A)^-1 by forward substitution: lane c < 16 computes column c,
@@ -297,8 +306,6 @@ __global__ __launch_bounds__(64) void gdn_prefill_prep_kernel(
         }
 #pragma unroll
         for (int t = 0; t < CH; ++t) rec[REC_T + t * CH + lane] = x[t] * be;
-        rec[REC_G + lane] = gl;
-        rec[REC_GE + lane] = ge;
     }
 }
 
@@ -316,7 +323,7 @@ struct ChunkOps {
     Run<AT, R> kx, qx;   // a operands of K S^T and Q S^T: token m, columns R g .. R g + R - 1
     Run<AT, NMT> ku[4];  // a operand of the update, step s: token 4g + s, columns NMT m .. + NMT
     AT v[RT][4];         // v[token 4g + j][state row of tile r], raw
-    f32x4 tb, pm;        // T diag(beta)[m][4g .. 4g+3], P[m][4g .. 4g+3]
+    f32x4 tb, pm;        // T diag(beta)[m][4g .. 4g+3], P (bf16 path: scale Gam)[m][4g .. 4g+3]
     f32x4 gm, ge;        // gamma and Gam_end of tokens 4g .. 4g+3
     float gend;          // gamma_15: decay of the whole chunk
     int nv;              // tokens of the chunk inside the sequence (1..16)
@@ -373,6 +380,9 @@ __device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
     f32x4 X[RT], Y[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) X[r] = Y[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // bf16 path: the record holds scale Gam for P; K Q^T (lane (g, m) ends with k_{4g+s} . q_m,
+    // exactly the a operand P[m][4g + s] needs) completes it.
+    f32x4 QKt = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kBf16Mma<D, AT>) {
         // Step s contracts over the lane's columns t = 8s .. 8s+7 of its run (state elements
         // (mt, i) = (t % NMT, t / NMT)); S' enters as three bf16 parts for X (which feeds the
@@ -399,6 +409,7 @@ __device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
                 Y[r] = mfma_k32(qa, bm, Y[r]);
                 X[r] = mfma_k32(ka, bl, X[r]);
             }
+            QKt = mfma_k32(ka, qa, QKt);
         }
     } else {
 #pragma unroll
@@ -434,10 +445,12 @@ __device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
 #pragma unroll
         for (int r = 0; r < RT; ++r) Dl[r] = mfma4(x.tb[s], Z[r][s], Dl[r]);
     // O = scale gamma c . Y' + P Delta.
+    f32x4 pm = x.pm;
+    if constexpr (kBf16Mma<D, AT>) pm *= QKt;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int r = 0; r < RT; ++r) O[r] = mfma4(x.pm[s], Dl[r][s], O[r]);
+        for (int r = 0; r < RT; ++r) O[r] = mfma4(pm[s], Dl[r][s], O[r]);
     // S' <- S' + K^T diag(Gam_end / c_new) Delta with c_new = gamma_15 c, tile by tile of 16 key
     // columns (after folding c_new into S' when it is out of range).
     float cn = x.gend * c;

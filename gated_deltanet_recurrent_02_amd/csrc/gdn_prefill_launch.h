@@ -12,6 +12,7 @@ namespace gdn {
 // Tokens per chunk, and floats per chunk record in the workspace:
 //   [0, 256)   T diag(beta): T = (I + A)^-1 of the chunk, columns scaled by beta   [t][s]
 //   [256, 512) P: scale * Gam_ts * (q_t . k_s) for s <= t, 0 above the diagonal     [t][s]
+//              (bf16 activations: scale * Gam_ts only; the state kernel applies q_t . k_s)
 //   [512, 528) gamma_t: alpha_0 ... alpha_t (alpha = 1 past the end of the sequence)
 //   [528, 544) Gam_end,t: alpha_{t+1} ... alpha_15
 constexpr int kPrefillChunk = 16;
