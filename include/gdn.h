@@ -181,7 +181,9 @@ gdn_status gdn_prefill_workspace_size(int64_t B, int32_t T, int32_t H, int32_t d
  * prefill: tokens are taken 16 at a time and the state is touched by dense products on the
  * matrix cores instead of one rank-1 update per token. The result is that of gdn_decode_step
  * on the same arguments up to fp32 rounding order (the state after the last token, and o for
- * every token); both read the state once and write it once.
+ * every token); both read the state once and write it once. One difference for non-finite
+ * inputs: a NaN or infinity in a token's k, q or v can also make the outputs of the earlier
+ * tokens of its 16-token chunk non-finite (other heads, sequences and chunks are unaffected).
  *
  *   q, k, v, alpha, beta, state, o, scale, act_dtype, state_dtype  as gdn_decode_step
  *   workspace        device buffer of at least gdn_prefill_workspace_size(...) bytes, owned

@@ -199,3 +199,27 @@ def test_offsets_beyond_2_31_elements():
     for n, (b, h) in enumerate(heads):
         check_state(S1[n][None], S_ref[n], torch.float32, what=f"state of head ({b}, {h})")
         check_o(o_s[n][None], o_ref[n, :, 0][None], torch.bfloat16)
+
+
+def test_nan_stays_in_its_head():
+    # A NaN in one head's initial state, and a NaN in another head's last token, reach only
+    # those heads. The state NaN stays in its row. The last-token NaN does not reach the earlier
+    # chunks of its head; within its own 16-token chunk the matrix products multiply it by
+    # the structural zeros of T diag(beta) and P (0 * NaN = NaN), so the earlier outputs of that
+    # chunk are not asserted (a documented property of the chunked form).
+    _announce("prefill NaN isolation")
+    x = synth.decode_inputs(3, 5, 64, 37, act="f32", seed=12)
+    x["state"][1, 2, 17, 5] = float("nan")
+    x["v"][2, 36, 4, 9] = float("nan")
+    S, o = gpu_prefill(x)
+    S, o = S.cpu(), o.cpu()
+    bad_s = torch.isnan(S).any(dim=(2, 3))
+    bad_o = torch.isnan(o).any(dim=(1, 3))
+    expect = torch.zeros(3, 5, dtype=torch.bool)
+    expect[1, 2] = True
+    expect[2, 4] = True
+    assert torch.equal(bad_s, expect) and torch.equal(bad_o, expect)
+    assert torch.isnan(S[1, 2]).any(dim=1).nonzero().flatten().tolist() == [17]
+    assert torch.isnan(o[1, :, 2]).any(dim=0).nonzero().flatten().tolist() == [17]
+    assert not torch.isnan(o[2, :32, 4]).any()
+    assert torch.isnan(o[2, 36, 4, 9])
