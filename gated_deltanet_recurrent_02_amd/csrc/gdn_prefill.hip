@@ -18,19 +18,27 @@
 // zero vectors, which makes their delta exactly 0.
 //
 // Two kernels:
-//   * prep (one wave per (b, h, chunk); all chunks in parallel): the chunk's Gram products
-//     K K^T and Q K^T on MFMA, the decays, T by forward substitution, written as one record of
-//     544 floats to the caller's workspace;
-//   * state (one wave per (b, h, 16 state rows), sequential over the chunks): the rows' state
-//     stays in registers for the whole call; per chunk five MFMA products (X, Q S^T, T diag(beta),
-//     P, the update), 104 v_mfma_f32_16x16x4f32 at D = 128, with the next chunk's operands
-//     loaded while the current one computes.
-// Matrix-core layout (v_mfma_f32_16x16x4f32, lane l = 16 g + n): operand a is A[l%16][l/16],
-// operand b is B[l/16][l%16], and the accumulator holds C[4 g + i][n], i = 0..3 (checked on the
-// device against a CPU product). The state's accumulator tiles of the update are arranged so that
-// the same registers are the b operand of the next chunk's K S^T and Q S^T: tile mt, element i
-// of lane (g, n) is S[row n][column (D/4) g + (D/16) i + mt], so each lane holds one state row's
-// contiguous run of D/4 columns and every load in the kernel is a contiguous vector.
+//   * prep (one wave per (b, h, chunk); all chunks in parallel): the chunk's Gram product K K^T
+//     on MFMA, the decays, T by forward substitution, and P (for bf16 activations only its
+//     factor scale Gam; see below), written as one record of 544 floats to the caller's
+//     workspace;
+//   * state (one wave per (b, h, 32 state rows: two tiles of 16), sequential over the chunks):
+//     the rows' state stays in registers for the whole call as S' = S / c (c a running product of
+//     chunk decays); per chunk the products X = K S'^T and Y = Q S'^T, Delta = T diag(beta) Z,
+//     O = Y + P Delta and the update, with the next chunk's operands loaded while the current
+//     one computes.
+// Matrix-core layout (lane l = 16 g + n; checked on the device against a CPU product): for
+// v_mfma_f32_16x16x4f32 operand a is A[l%16][l/16], operand b is B[l/16][l%16]; the 16 x 16 x 32
+// and 16 x 16 x 16 bf16 forms hold 8 and 4 consecutive k per lane (k = 8 (l/16) + e, 4 (l/16)
+// + e); all accumulate into C[4 g + i][n], i = 0..3. The state's accumulator tiles of the update
+// are arranged so that the same registers are the b operand of the next chunk's K S'^T and
+// Q S'^T: tile mt, element i of lane (g, n) is S[row n][column (D/4) g + (D/16) i + mt], so each
+// lane holds one state row's contiguous run of D/4 columns and every load is a contiguous vector.
+// For bf16 activations (D >= 32) k and q are exact bf16 operands of the bf16 matrix cores and
+// the fp32 state enters as three bf16 parts whose sum is exact (two for Q S'^T, whose result is
+// rounded to bf16); other activation types use the fp32 form. A NaN or infinity in a token's k,
+// q or v also reaches the earlier outputs of its own chunk (products with the structural zeros
+// of T diag(beta) and P); finite inputs are exact to fp32 rounding.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
