@@ -13,6 +13,9 @@ Integer/byte work (the conv state, a move of raw bf16 inputs) must match bit for
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -86,6 +89,22 @@ def oracle_decode(x: dict, scale: float = 1.0, heads=None):
     S0 = f64(x["state"][bt, ht])[:, None]
     S, o = oracle.gdn_decode(q, k, v, al, be, S0, scale=scale)
     return S[:, 0], o[:, :, 0]
+
+
+def oracle_decode_all(x: dict, scale: float = 1.0, workers: int = 0):
+    """The oracle on every (b, h) head, the heads split over a thread pool (the C oracle runs
+    outside the GIL). Returns (state [B,H,dv,dk], o [B,T,H,dv]) like oracle_decode(x)."""
+    B, H = x["B"], x["H"]
+    workers = workers or min(16, os.cpu_count() or 1)
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    groups = [g for g in np.array_split(np.asarray(pairs), workers) if len(g)]
+    with ThreadPoolExecutor(len(groups)) as ex:
+        parts = list(ex.map(lambda g: oracle_decode(x, scale, heads=[tuple(p) for p in g]), groups))
+    S = np.concatenate([p[0] for p in parts])           # [B*H, dv, dk] in (b, h) order
+    o = np.concatenate([p[1] for p in parts])           # [B*H, T, dv]
+    T, dv = o.shape[1], o.shape[2]
+    return (S.reshape(B, H, *S.shape[1:]),
+            o.reshape(B, H, T, dv).transpose(0, 2, 1, 3))
 
 
 def sample_heads(B: int, H: int, n: int, seed: int = 0):
