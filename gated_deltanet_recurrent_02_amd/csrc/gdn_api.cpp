@@ -63,6 +63,8 @@ gdn_status check_shape(const char* fn, int64_t B, int32_t T, int32_t H, int32_t 
                         std::to_string(dk) + " dv=" + std::to_string(dv));
     if (B * (int64_t)H >= (int64_t(1) << 31))
         return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": B * H must be < 2^31");
+    if (B * (int64_t)H * gdn::kThreadsPerHeadPerDim * dk >= gdn::kMaxWorkItems)
+        return fail(GDN_ERR_UNSUPPORTED, std::string(fn) + ": B * H * 8 * dk must be < 2^32 (one dispatch)");
     return GDN_OK;
 }
 
@@ -329,8 +331,8 @@ gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
     if (!valid_dtype(act_dtype) || !valid_dtype(state_dtype))
         return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": bad dtype");
     if (B == 0 || T == 0) return GDN_OK;
-    if (B * (int64_t)H * gdn::prefill_chunks(T) >= (int64_t(1) << 31))
-        return fail(GDN_ERR_UNSUPPORTED, std::string(fn) + ": B * H * ceil(T / 16) must be < 2^31");
+    if (B * (int64_t)H * gdn::prefill_chunks(T) * gdn::kPrefillWaveThreads >= gdn::kMaxWorkItems)
+        return fail(GDN_ERR_UNSUPPORTED, std::string(fn) + ": B * H * ceil(T / 16) must be < 2^26 (one dispatch)");
     s = check_ptrs(fn, {{"q", q}, {"k", k}, {"v", v}, {"alpha", alpha}, {"beta", beta},
                         {"state", state}, {"o", o}, {"workspace", workspace}});
     if (s != GDN_OK) return s;

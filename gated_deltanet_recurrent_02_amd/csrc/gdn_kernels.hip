@@ -306,15 +306,21 @@ __device__ __forceinline__ void store_state(typename G::ST* __restrict__ Sg, int
 
 // ------------------------------------------------------------------------ one token
 
-// Row totals shared by both token forms: kq = k_raw . q_raw and, per pass, u = S k_raw and
-// w = S q_raw (S as held in registers), reduced over the row's lanes.
+// kq = k_raw . q_raw of one token from the lane's E columns, reduced over the row's lanes.
 template <class G>
-__device__ __forceinline__ float row_dots(const float (&S)[G::P][G::E], const float (&kk)[G::E],
-                                          const float (&qq)[G::E], float (&u)[G::P],
-                                          float (&w)[G::P]) {
+__device__ __forceinline__ float row_kq(const float (&kk)[G::E], const float (&qq)[G::E]) {
     float kq = 0.f;
 #pragma unroll
     for (int e = 0; e < G::E; ++e) kq = fmaf(kk[e], qq[e], kq);
+    return row_sum<G::LPR>(kq);
+}
+
+// Row totals shared by both token forms: per pass, u = S k_raw and w = S q_raw (S as held in
+// registers), reduced over the row's lanes.
+template <class G>
+__device__ __forceinline__ void row_dots(const float (&S)[G::P][G::E], const float (&kk)[G::E],
+                                         const float (&qq)[G::E], float (&u)[G::P],
+                                         float (&w)[G::P]) {
 #pragma unroll
     for (int p = 0; p < G::P; ++p) {
         float su = 0.f, sw = 0.f;
@@ -326,13 +332,11 @@ __device__ __forceinline__ float row_dots(const float (&S)[G::P][G::E], const fl
         u[p] = su;
         w[p] = sw;
     }
-    kq = row_sum<G::LPR>(kq);
 #pragma unroll
     for (int p = 0; p < G::P; ++p) {
         u[p] = row_sum<G::LPR>(u[p]);
         w[p] = row_sum<G::LPR>(w[p]);
     }
-    return kq;
 }
 
 // What a token step returns on the lane with l == p of each row group, for the row of pass p:
@@ -341,15 +345,16 @@ struct RowOut {
     float o, dk;
 };
 
-// One token with S held as is. k = kf k_raw, q = qf q_raw:
+// One token with S held as is. k = kf k_raw, q = qf q_raw, kq = k_raw . q_raw:
 //   u = kf (S k_raw);  delta = beta (v - alpha u);  S <- alpha S + (delta kf) k_raw;
-//   o = qf (alpha (S q_raw) + (delta kf) (k_raw . q_raw)).
+//   o = qf (alpha (S q_raw) + (delta kf) kq).
 template <class G>
 __device__ __forceinline__ RowOut token_plain(float (&S)[G::P][G::E], const float (&kk)[G::E],
                                              const float (&qq)[G::E], const float (&vr)[G::P],
-                                             float a, float bt, float kf, float qf, int l) {
+                                             float a, float bt, float kf, float qf, float kq,
+                                             int l) {
     float u[G::P], w[G::P];
-    const float kq = row_dots<G>(S, kk, qq, u, w);
+    row_dots<G>(S, kk, qq, u, w);
     RowOut r = {0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < G::P; ++p) {
@@ -372,10 +377,10 @@ __device__ __forceinline__ RowOut token_plain(float (&S)[G::P][G::E], const floa
 template <class G>
 __device__ __forceinline__ RowOut token_scaled(float (&S)[G::P][G::E], const float (&kk)[G::E],
                                               const float (&qq)[G::E], const float (&vr)[G::P],
-                                              float a, float bt, float kf, float qf, float c,
-                                              float cn, int l) {
+                                              float a, float bt, float kf, float qf, float kq,
+                                              float c, float cn, int l) {
     float u[G::P], w[G::P];
-    const float kq = row_dots<G>(S, kk, qq, u, w);
+    row_dots<G>(S, kk, qq, u, w);
     const float kc = kf * c, inv_cn = __builtin_amdgcn_rcpf(cn);
     RowOut r = {0.f, 0.f};
 #pragma unroll
@@ -432,6 +437,37 @@ struct TokenOperands {
     }
 };
 
+// k_raw . q_raw of every token of a round, formed once per wave (with several tokens per round):
+// the 64 / TCH lanes of group j sum token j's products, so token tt reads its value from lane
+// tt * (64 / TCH). Lanes of tokens past the round's count read stale LDS and are never used.
+template <class G>
+__device__ __forceinline__ float round_kq(const TokLds<G::D, G::TCH>& L, int lane) {
+    constexpr int LT = 64 / G::TCH, EL = G::D / LT, VK = EL < 4 ? EL : 4;
+    static_assert(LT == 4 || LT == 8 || LT == 16, "token groups of 4, 8 or 16 lanes");
+    static_assert(EL % VK == 0 && (VK == 2 || VK == 4), "columns per lane");
+    const int tt = lane / LT, j = lane % LT;
+    float kq = 0.f;
+    // lane j sums the VK-column blocks j, j + LT, j + 2 LT, ... of its token
+#pragma unroll
+    for (int e = 0; e < EL; e += VK) {
+        const int at = e * LT + VK * j;
+        if constexpr (VK == 4) {
+            const float4 k4 = *(const float4*)&L.k[tt][at];
+            const float4 q4 = *(const float4*)&L.q[tt][at];
+            kq = fmaf(k4.x, q4.x, kq);
+            kq = fmaf(k4.y, q4.y, kq);
+            kq = fmaf(k4.z, q4.z, kq);
+            kq = fmaf(k4.w, q4.w, kq);
+        } else {
+            const float2 k2 = *(const float2*)&L.k[tt][at];
+            const float2 q2 = *(const float2*)&L.q[tt][at];
+            kq = fmaf(k2.x, q2.x, kq);
+            kq = fmaf(k2.y, q2.y, kq);
+        }
+    }
+    return row_sum<LT>(kq);
+}
+
 // The recurrence for `nt` staged tokens. `obase` points at o[b][t0][h][0]; consecutive tokens
 // are `ostride` elements apart. The row of pass p is row0 + p*RPP with row0 = rbase + g, rbase
 // the wave's first row; the lane with l == p of row group g writes o for that row, so one
@@ -439,6 +475,10 @@ struct TokenOperands {
 // With MULTI the registers hold S / c and `c` carries the scale across rounds: tokens run in
 // the scaled form while c alpha stays in [2^-64, 2^64]; a token that would leave that range
 // (alpha = 0, very small or large, NaN) folds c back into the registers and runs plainly.
+// The two forms sit in one loop, except with DELTA: on MI355X the one-loop form runs the
+// 16-bit-state decode and fused calls 4-5% faster (the compiler keeps the state registers in
+// place across tokens instead of copying them), while the verify kernels run faster with the
+// scaled tokens in an inner loop of their own.
 // With DELTA, each token's write coefficients dk (one per row) also go to `dbase`, laid out
 // like o but in fp32.
 template <class G, bool MULTI, typename AT, bool DELTA = false>
@@ -454,31 +494,40 @@ __device__ __forceinline__ void recur_tokens(float (&S)[G::P][G::E],
             if constexpr (DELTA) dbase[at] = r.dk;
         }
     };
+    constexpr bool kRoundKq = G::TCH >= 4;
+    float kqv = 0.f;
+    if constexpr (kRoundKq) kqv = round_kq<G>(L, g * G::LPR + l);
+    auto kq_of = [&](int tt, const TokenOperands<G>& t) {
+        if constexpr (kRoundKq) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                __builtin_bit_cast(int, kqv), tt * (64 / G::TCH)));
+        } else {
+            return row_kq<G>(t.kk, t.qq);
+        }
+    };
     if constexpr (!MULTI) {
         for (int tt = 0; tt < nt; ++tt) {
             TokenOperands<G> t;
             t.load(L, tt, row0, l);
-            put_o(tt, token_plain<G>(S, t.kk, t.qq, t.vr, t.a, t.bt, t.kf, t.qf, l));
+            put_o(tt, token_plain<G>(S, t.kk, t.qq, t.vr, t.a, t.bt, t.kf, t.qf, kq_of(tt, t), l));
         }
     } else {
-        int tt = 0;
-        while (tt < nt) {
-            for (; tt < nt; ++tt) {
-                TokenOperands<G> t;
-                t.load(L, tt, row0, l);
-                const float cn = c * t.a;
-                if (!(cn >= 0x1p-64f && cn <= 0x1p64f)) break;
-                put_o(tt, token_scaled<G>(S, t.kk, t.qq, t.vr, t.a, t.bt, t.kf, t.qf, c, cn, l));
-                c = cn;
-            }
-            if (tt < nt) {
-                TokenOperands<G> t;
-                t.load(L, tt, row0, l);
-                if (c != 1.0f) scale_state<G>(S, c);
+        for (int tt = 0; tt < nt; ++tt) {
+            TokenOperands<G> t;
+            t.load(L, tt, row0, l);
+            float a = t.a, cn = c * a;
+            if (!(cn >= 0x1p-64f && cn <= 0x1p64f)) {
+                // Fold c and then this token's alpha into the registers (two roundings, as
+                // the plain form takes them); the token then runs with c = alpha = 1.
+                scale_state<G>(S, c);
+                scale_state<G>(S, a);
+                a = 1.0f;
                 c = 1.0f;
-                put_o(tt, token_plain<G>(S, t.kk, t.qq, t.vr, t.a, t.bt, t.kf, t.qf, l));
-                ++tt;
+                cn = 1.0f;
             }
+            put_o(tt, token_scaled<G>(S, t.kk, t.qq, t.vr, a, t.bt, t.kf, t.qf, kq_of(tt, t), c,
+                                      cn, l));
+            c = cn;
         }
     }
 }
@@ -841,6 +890,7 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
     AT* o = (AT*)a.o;
     float scale = a.scale;
     void* args[] = {&T, &H, &q, &k, &v, &alpha, &beta, &state, &o, &scale};
+    static_assert((int64_t)G::NT * G::SPLIT <= kThreadsPerHeadPerDim * G::D, "threads per head");
     return hipLaunchKernel((const void*)gdn_decode_kernel<G, MULTI, AT>,
                            dim3((unsigned)(a.B * a.H * G::SPLIT)), dim3(G::NT), args, 0, s);
 }
@@ -863,6 +913,7 @@ hipError_t launch_verify_g(const VerifyArgs& a, hipStream_t s) {
     float scale = a.scale;
     void* args[] = {&T, &H, &q, &k, &v, &alpha, &beta, &state, &Tp, &n_prev, &k_prev,
                     &alpha_prev, &dk_prev, &o, &dk_out, &scale};
+    static_assert((int64_t)G::NT * G::SPLIT <= kThreadsPerHeadPerDim * G::D, "threads per head");
     return hipLaunchKernel((const void*)gdn_verify_kernel<G, AT>,
                            dim3((unsigned)(a.B * a.H * G::SPLIT)), dim3(G::NT), args, 0, s);
 }
@@ -880,6 +931,7 @@ hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
     uint16_t* o = (uint16_t*)a.o;
     float scale = a.scale, eps = a.l2_eps;
     void* args[] = {&T, &H, &qkv, &cs, &w, &cb, &al, &bl, &state, &o, &scale, &eps};
+    static_assert((int64_t)G::NT * 1 <= kThreadsPerHeadPerDim * G::D, "threads per head");
     return hipLaunchKernel((const void*)gdn_conv_gate_decode_kernel<G, MULTI>,
                            dim3((unsigned)(a.B * a.H)), dim3(G::NT), args, 0, s);
 }
@@ -894,7 +946,10 @@ constexpr int max_int(int a, int b) { return a > b ? a : b; }
 //  * one token, bf16 state: all rows of a head in one workgroup, 8 rows per wave;
 //  * several tokens (and the fused path): the per-token arithmetic is repeated on registers,
 //    so occupancy and instruction count decide: 16 rows per wave, one workgroup per head,
-//    8 lanes per row where it saves reduction steps (bf16 state, fused prologue).
+//    8 lanes per row where it saves reduction steps (bf16 state, fused prologue);
+//  * several tokens, fp32 state, decode: one wave per workgroup again (16 rows, the 8 tiles
+//    of a head kept on one XCD so its q and k come from one L2): 2% faster than a workgroup
+//    per head at B=256 H=48 D=128 T=4, where the verify kernel is 3% slower with it.
 template <int D, typename ST> struct DecodeOneToken {  // 2-byte states
     using G = Geo<D, ST, D / 8, 1, 1, true, true>;
 };
@@ -906,6 +961,13 @@ template <int D, typename ST> struct DecodeTokens {  // 2-byte states
     using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
 };
 template <int D> struct DecodeTokens<D, float> {
+    using G = Geo<D, float, 1, max_int(1, D / 16), 8, true, true, 2, 16>;
+};
+
+template <int D, typename ST> struct VerifyTokens {  // 2-byte states
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
+};
+template <int D> struct VerifyTokens<D, float> {
     using G = Geo<D, float, max_int(1, D / 16), 1, 8, true, true, 0, 16>;
 };
 
@@ -939,7 +1001,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
 
 template <int D, typename ST>
 hipError_t launch_verify_s(const VerifyArgs& a, hipStream_t s) {
-    using G = typename DecodeTokens<D, ST>::G;
+    using G = typename VerifyTokens<D, ST>::G;
     switch (a.act) {
         case DType::F32: return launch_verify_g<G, float>(a, s);
         case DType::BF16: return launch_verify_g<G, uint16_t>(a, s);

@@ -10,6 +10,12 @@ namespace gdn {
 
 enum class DType : int { F32 = 0, BF16 = 1, F16 = 2 };
 
+// A dispatch covers fewer than 2^32 work-items. Every decode, verify and fused launch runs at
+// most kThreadsPerHeadPerDim * D threads per head (checked where each kernel is instantiated),
+// so B * H * 8 * D < 2^32 makes every launch fit.
+constexpr int64_t kThreadsPerHeadPerDim = 8;
+constexpr int64_t kMaxWorkItems = int64_t(1) << 32;
+
 struct DecodeArgs {
     int64_t B;
     int32_t T, H, D;          // D = dk = dv

@@ -599,6 +599,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
                                    dim3((unsigned)(heads * nch)), dim3(64), pargs, 0, s);
     if (e != hipSuccess) return e;
     constexpr int RT = (D >= 32) ? 2 : 1;  // 16-row tiles per wave
+    static_assert(D / (16 * RT) * 64 <= kThreadsPerHeadPerDim * D, "threads per head");
     const unsigned grid = (unsigned)(heads * (D / (16 * RT)));
     int remap = (grid % 8u == 0u) ? 1 : 0;
     void* sargs[] = {&T, &H, &nch, &q, &k, &v, &wsc, &state, &o, &scale, &remap};

@@ -34,7 +34,11 @@ struct PrefillArgs {
     float* ws;                // [B][H][ceil(T/16)][kPrefillRecordFloats]
 };
 
-// Workgroups each kernel launches (both must be < 2^31; checked by the caller).
+// Chunks per sequence. The prep kernel launches one 64-thread workgroup per (sequence, head,
+// chunk), which the caller keeps below 2^32 work-items; the state kernel runs at most 4
+// workgroups of 64 threads per head (D / 32 at D >= 32, one at D = 16), within the decode
+// bound of 8 D threads per head that the caller checks too.
+constexpr int64_t kPrefillWaveThreads = 64;
 inline int64_t prefill_chunks(int32_t T) { return (T + kPrefillChunk - 1) / kPrefillChunk; }
 
 // Enqueues the prep kernel, then the state kernel; nothing is synchronised.

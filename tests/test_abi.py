@@ -106,6 +106,7 @@ def last_error():
     (dict(o=P(80 * MB + 1024)), INVALID, "o overlaps state"),
     (dict(state=P(32 * MB)), INVALID, "state overlaps v"),
     (dict(B=1 << 26, H=32), INVALID, "B * H"),
+    (dict(B=1 << 20, H=1 << 5), UNSUPPORTED, "B * H * 8 * dk"),   # 2^32 work-items
 ])
 @fake_ptrs
 def test_decode_step_rejects(kw, status, msg):
@@ -267,7 +268,9 @@ def test_prefill_workspace_size():
     (dict(ws=P(16 * MB)), INVALID, "workspace overlaps k"),
     (dict(o=P(200 * MB)), INVALID, "o overlaps workspace"),
     (dict(state=P(200 * MB)), INVALID, "state overlaps workspace"),
-    (dict(B=1 << 20, H=1 << 10, T=64), UNSUPPORTED, "ceil(T / 16)"),
+    (dict(B=1 << 20, H=1 << 5), UNSUPPORTED, "B * H * 8 * dk"),
+    (dict(B=1 << 10, H=1 << 10, T=2048), UNSUPPORTED, "ceil(T / 16)"),  # 2^33 prep threads
+    (dict(B=1 << 10, H=1 << 9, T=2032, ws_bytes=1000), INVALID, "needed"),  # 127 * 2^25: fits
 ])
 @fake_ptrs
 def test_prefill_rejects(kw, status, msg):
