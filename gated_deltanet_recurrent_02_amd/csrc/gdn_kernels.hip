@@ -714,18 +714,46 @@ __global__ __launch_bounds__(G::NT) void gdn_verify_kernel(
         np = __builtin_amdgcn_readfirstlane(n_prev[b]);
         np = np < 0 ? 0 : (np > Tp ? Tp : np);
     }
-    for (int t = 0; t < np; ++t) {
+    // The registers hold S / cc with cc the product of the alphas replayed so far, so each
+    // replayed token costs one FMA per element (S' <- S' + (dk / cc') k, cc' = cc alpha); cc
+    // is folded back when it would leave [2^-64, 2^64] and before the store. The next token's
+    // operands are loaded before this token's update (the index is clamped, so the loads are
+    // unconditional).
+    struct Replay {
+        float kk[G::E], dl[G::P], a;
+    };
+    auto load_replay = [&](int t, Replay& r) {
         const size_t tok = ((size_t)b * Tp + t) * H + h;
-        float kk[G::E], dl[G::P];
 #pragma unroll
-        for (int e = 0; e < G::E; ++e) kk[e] = act_to_f32(k_prev[tok * D + G::col(l, e)]);
+        for (int e = 0; e < G::E; ++e) r.kk[e] = act_to_f32(k_prev[tok * D + G::col(l, e)]);
 #pragma unroll
-        for (int p = 0; p < G::P; ++p) dl[p] = dk_prev[tok * D + row0 + p * G::RPP];
-        const float a = uniform(alpha_prev[tok]);
+        for (int p = 0; p < G::P; ++p) r.dl[p] = dk_prev[tok * D + row0 + p * G::RPP];
+        r.a = uniform(alpha_prev[tok]);
+    };
+    float cc = 1.0f;
+    if (np > 0) {
+        Replay cur;
+        load_replay(0, cur);
+        for (int t = 0; t < np; ++t) {
+            Replay nxt;
+            load_replay(min(t + 1, np - 1), nxt);
+            float cn = cc * cur.a;
+            if (!(cn >= 0x1p-64f && cn <= 0x1p64f)) {
+                scale_state<G>(S, cc);
+                scale_state<G>(S, cur.a);
+                cn = 1.0f;
+            }
+            const float inv_cn = __builtin_amdgcn_rcpf(cn);
 #pragma unroll
-        for (int p = 0; p < G::P; ++p)
+            for (int p = 0; p < G::P; ++p) {
+                const float coef = cur.dl[p] * inv_cn;
 #pragma unroll
-            for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(dl[p], kk[e], a * S[p][e]);
+                for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(coef, cur.kk[e], S[p][e]);
+            }
+            cc = cn;
+            cur = nxt;
+        }
+        if (cc != 1.0f) scale_state<G>(S, cc);
     }
     if (np > 0) store_state<G>(Sg, row0, l, S);
 
@@ -835,7 +863,9 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
                         y = fmaf(tap[s][3], bf16_to_f32(x), y);
                         y += bias[s];
                         win[s][0] = win[s][1]; win[s][1] = win[s][2]; win[s][2] = x;
-                        dst[tt * D] = y / (1.0f + expf(-y));
+                        // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
+                        dst[tt * D] = y * __builtin_amdgcn_rcpf(
+                                              1.0f + __builtin_amdgcn_exp2f(-y * 1.44269504f));
                     }
                 }
             }
