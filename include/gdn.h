@@ -28,7 +28,8 @@
  *  - Empty work. B == 0 or T == 0 is a valid no-op (GDN_OK, nothing enqueued); pointers may
  *    then be NULL.
  *  - Shapes. dk == dv, one of 16, 32, 64, 128 (others return GDN_ERR_UNSUPPORTED);
- *    H >= 1; B * H < 2^31.
+ *    H >= 1; B * H < 2^31; B * H * 8 * dk < 2^32, i.e. fewer than 4,194,304 heads at dk = 128
+ *    (every launch is one dispatch; GDN_ERR_UNSUPPORTED beyond).
  *  - Reentrancy. Calls on different buffers may run concurrently from any threads. Two calls
  *    that update the same state concurrently race.
  */
@@ -192,7 +193,9 @@ gdn_status gdn_prefill_workspace_size(int64_t B, int32_t T, int32_t H, int32_t d
  *                    at once need two workspaces.
  *   workspace_bytes  its size in bytes
  * Errors: as gdn_decode_step; GDN_ERR_INVALID_ARGUMENT also for a workspace smaller than
- * required; GDN_ERR_UNSUPPORTED when B * H * ceil(T / 16) >= 2^31.
+ * required; GDN_ERR_UNSUPPORTED when B * H * ceil(T / 16) * 64 >= 2^32 (the prep kernel's
+ * single dispatch). For runs of up to 16 tokens gdn_decode_step is faster (up to 32 with fp32
+ * states at B * H >= 1536); this call always runs the chunked form.
  */
 gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                        const void* q, const void* k, const void* v, gdn_dtype act_dtype,
