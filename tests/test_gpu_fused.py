@@ -105,6 +105,25 @@ def test_identity_taps_and_zero_logit_gates():
     check_o(f64(o), o_ref, torch.bfloat16)
 
 
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_extreme_gate_logits_fold_the_scale(sdt):
+    # Decay logits that drive alpha to 0 (a = 200: exp(-200) underflows fp32), to ~9e-27
+    # (a = 60, below 2^-64 whatever the running scale) and to 1 (a = -200), over 20 tokens (three
+    # staging rounds): the running scale leaves [2^-64, 2^64] and is folded into the state.
+    _announce(f"fused extreme gate logits state={sdt}")
+    x = synth.fused_inputs(2, 3, 64, 20, state_dtype=sdt, seed=23)
+    a = x["a_logit"]
+    a[0, 3, 0] = 200.0
+    a[0, 10:, 1] = 60.0
+    a[1, :, 2] = -200.0
+    a[1, ::4, 0] = 60.0
+    S, o, cs = gpu_fused(x)
+    S_ref, o_ref, cs_ref = oracle_fused(x)
+    assert np.array_equal(f64(cs), cs_ref)
+    check_state(f64(S), S_ref, DT[sdt])
+    check_o(f64(o), o_ref, torch.bfloat16)
+
+
 def test_conv_state_roll_for_short_calls():
     # T = 1 and 2 take the oldest entries of the new conv state from the old one.
     for T in (1, 2):

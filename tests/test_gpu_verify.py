@@ -110,6 +110,29 @@ def test_full_acceptance_equals_plain_step():
     assert torch.equal(o_ver.view(torch.int16), o_plain.view(torch.int16))
 
 
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_replay_folds_out_of_range_decays(sdt):
+    # Replayed prefixes whose running product of alphas leaves [2^-64, 2^64]: alpha = 50 for
+    # 12 tokens (50^12 > 2^64), alpha = 0 mid-prefix, alpha = 1e-30 every third token; 20
+    # drafted tokens, prefixes of 9 to 20.
+    _announce(f"verify replay fold paths state={sdt}")
+    B, H, D, T = 4, 3, 64, 20
+    x = synth.decode_inputs(B, H, D, T, state_dtype=sdt, alpha_shift=-1.0, seed=45)
+    a = x["alpha"]
+    a[0, :12, 0] = 50.0
+    a[1, 5, 1] = 0.0
+    a[2, ::3, 2] = 1e-30
+    n = torch.tensor([12, 20, 17, 9], dtype=torch.int32)
+    g = to_dev(x)
+    state = g["state"]
+    _, d = gdn.decode_verify(*_tokens(g), state)
+    empty = tuple(t[:, :0].contiguous() for t in _tokens(g))
+    gdn.decode_verify(*empty, state, prev=(n.cuda(), g["k"], g["alpha"], d))
+    torch.cuda.synchronize()
+    S_ref = _oracle_prefix(f64(x["state"]), x, n.tolist())
+    check_state(f64(state), S_ref, DT[sdt], what="committed state")
+
+
 def test_n_prev_is_clamped():
     _announce("verify clamps n_prev")
     x = to_dev(synth.decode_inputs(2, 3, 32, 3, seed=44))
