@@ -979,7 +979,11 @@ constexpr int max_int(int a, int b) { return a > b ? a : b; }
 //    8 lanes per row where it saves reduction steps (bf16 state, fused prologue);
 //  * several tokens, fp32 state, decode: one wave per workgroup again (16 rows, the 8 tiles
 //    of a head kept on one XCD so its q and k come from one L2): 2% faster than a workgroup
-//    per head at B=256 H=48 D=128 T=4, where the verify kernel is 3% slower with it.
+//    per head at B=256 H=48 D=128 T=4, where the verify kernel is 3% slower with it;
+//  * fused path, fp32 state: 4 waves of 32 rows per head (190 VGPRs, two workgroups per CU):
+//    2.5% faster than 8 waves of 16 rows at B=256 H=48 D=128 T=4; 16-bit states lose 9% with
+//    it. The fused kernel needs the whole head in one workgroup (the conv state of the q and
+//    k channels is read and rewritten by it).
 template <int D, typename ST> struct DecodeOneToken {  // 2-byte states
     using G = Geo<D, ST, D / 8, 1, 1, true, true>;
 };
@@ -1001,8 +1005,11 @@ template <int D> struct VerifyTokens<D, float> {
     using G = Geo<D, float, max_int(1, D / 16), 1, 8, true, true, 0, 16>;
 };
 
-template <int D, typename ST> struct FusedTokens {
+template <int D, typename ST> struct FusedTokens {  // 2-byte states
     using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
+};
+template <int D> struct FusedTokens<D, float> {
+    using G = Geo<D, float, max_int(1, D / 32), 1, 8, true, true, 0, 8>;
 };
 
 template <int D, typename ST, typename AT>
