@@ -44,15 +44,45 @@ MALL_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 _CSRC = os.path.join(ROOT, "gated_deltanet_recurrent_02_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_kernels.hip", "gdn_launch.h")]
-PREFILL_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_prefill.hip", "gdn_prefill_launch.h")]
+PREFILL_SOURCES = [os.path.join(_CSRC, f)
+                   for f in ("gdn_prefill.hip", "gdn_prefill_launch.h", "gdn_launch.h")]
+
+
+def code_text(src: str) -> str:
+    """C++ source without its comments, whitespace runs collapsed: what the compiler sees,
+    so that editing a comment does not count as changing a kernel. String and character
+    literals are kept verbatim."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
 
 
 def kernel_source_hash(prefill: bool = False) -> str:
-    """Hash of the kernel sources a workload runs (decode kernels or the prefill kernels)."""
+    """Hash of the code a workload runs: the kernel sources (decode kernels or the prefill
+    kernels) as code_text, plus the compiler flags they are built with."""
+    from gated_deltanet_recurrent_02_amd import build as gdn_build
     h = hashlib.sha256()
     for p in (PREFILL_SOURCES if prefill else KERNEL_SOURCES):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
+    h.update(" ".join(gdn_build.HIPFLAGS).encode())
     return h.hexdigest()[:16]
 
 

@@ -472,13 +472,12 @@ __device__ __forceinline__ float round_kq(const TokLds<G::D, G::TCH>& L, int lan
 // are `ostride` elements apart. The row of pass p is row0 + p*RPP with row0 = rbase + g, rbase
 // the wave's first row; the lane with l == p of row group g writes o for that row, so one
 // store covers all the wave's rows.
-// With MULTI the registers hold S / c and `c` carries the scale across rounds: tokens run in
-// the scaled form while c alpha stays in [2^-64, 2^64]; a token that would leave that range
-// (alpha = 0, very small or large, NaN) folds c back into the registers and runs plainly.
-// The two forms sit in one loop, except with DELTA: on MI355X the one-loop form runs the
-// 16-bit-state decode and fused calls 4-5% faster (the compiler keeps the state registers in
-// place across tokens instead of copying them), while the verify kernels run faster with the
-// scaled tokens in an inner loop of their own.
+// With MULTI the registers hold S / c and `c` carries the scale across rounds; every token
+// runs the scaled form. A token whose c alpha would leave [2^-64, 2^64] (alpha = 0, very small
+// or large, NaN) first multiplies the registers by c and then by its alpha, and runs with
+// c = alpha = 1 (exactly the plain form's update). One loop body with the state defined only
+// by the update's FMAs lets the compiler keep the state registers in place across tokens (two
+// inlined token forms made it copy them every token and raised the register count).
 // With DELTA, each token's write coefficients dk (one per row) also go to `dbase`, laid out
 // like o but in fp32.
 template <class G, bool MULTI, typename AT, bool DELTA = false>
