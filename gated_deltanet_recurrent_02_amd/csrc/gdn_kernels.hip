@@ -26,7 +26,8 @@
 // factors (1/|k|, scale/|q| in the fused path) multiply the row totals. For several tokens the
 // registers hold S' = S / c with c the running product of alpha over the call's tokens, which
 // turns the update into one FMA per element (S' += (delta / c) k); c is folded back before the
-// store, or earlier if it leaves [2^-64, 2^64] (see token_step).
+// store, or earlier if it leaves [2^-64, 2^64] (see recur_tokens). With several tokens per
+// staged round the wave also forms each token's k . q once instead of once per row.
 // The fused kernel replaces the staging by the conv (kernel 4) + SiLU + L2-norm + gate
 // prologue of the same chain, computed by the workgroup for the 3*D channels its head owns; it
 // is also the only reader and writer of those channels' conv state.
