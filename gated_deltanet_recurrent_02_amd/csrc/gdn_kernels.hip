@@ -973,7 +973,9 @@ constexpr int max_int(int a, int b) { return a > b ? a : b; }
 //  * one token, fp32 state: one wave per workgroup, 8 rows (4 KiB) per wave, nontemporal
 //    state loads and stores -- 79% of HBM peak; larger workgroups synchronise their waves'
 //    load/store phases and lose 5-15%;
-//  * one token, bf16 state: all rows of a head in one workgroup, 8 rows per wave;
+//  * one token, bf16 state: all rows of a head in one workgroup, 8 rows per wave, 8 lanes per
+//    row (two 16-byte loads per lane and row): 140 -> 130 us at B=256 H=48 D=128 against 16
+//    lanes per row (fp32 states show no difference);
 //  * several tokens (and the fused path): the per-token arithmetic is repeated on registers,
 //    so occupancy and instruction count decide: 16 rows per wave, one workgroup per head,
 //    8 lanes per row where it saves reduction steps (bf16 state, fused prologue);
@@ -985,7 +987,7 @@ constexpr int max_int(int a, int b) { return a > b ? a : b; }
 //    it. The fused kernel needs the whole head in one workgroup (the conv state of the q and
 //    k channels is read and rewritten by it).
 template <int D, typename ST> struct DecodeOneToken {  // 2-byte states
-    using G = Geo<D, ST, D / 8, 1, 1, true, true>;
+    using G = Geo<D, ST, D / 8, 1, 1, true, true, 0, 8>;
 };
 template <int D> struct DecodeOneToken<D, float> {
     using G = Geo<D, float, 1, D / 8, 1, true, true>;
