@@ -71,6 +71,46 @@ def test_t4_on_full_heads_all_state_dtypes():
         check_o(f64(o), o_ref, torch.bfloat16)
 
 
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("T", [2, 3, 5, 8])
+def test_multi_token_bf16_every_head_dim(D, T):
+    # bf16 state and activations, 2 to 8 tokens (one staged round), every head dim; all heads
+    # against the oracle.
+    _announce(f"multi-token bf16 decode B=2 H=3 D={D} T={T}")
+    x = synth.decode_inputs(2, 3, D, T, state_dtype="bf16", alpha_shift=-1.0, state_std=0.3,
+                            seed=100 + D + T)
+    S, o = gpu_decode(x, scale=0.6)
+    S_ref, o_ref = oracle_decode(x, scale=0.6)
+    check_state(f64(S), S_ref, torch.bfloat16)
+    check_o(f64(o), o_ref, torch.bfloat16)
+
+
+def test_multi_token_bf16_gate_edges_and_nan_row():
+    # bf16 state, 8 tokens: alpha = 0 mid-call, alpha = 1e-30 every other token and alpha = 50
+    # throughout (the running scale leaves [2^-64, 2^64] both ways), beta = 0, each on its own
+    # head; a NaN in one state row stays in that row of that head.
+    _announce("multi-token bf16 decode gate edges")
+    x = synth.decode_inputs(2, 4, 128, 8, state_dtype="bf16", alpha_shift=-1.0, state_std=0.3,
+                            seed=120)
+    x["alpha"][0, 3, 0] = 0.0
+    x["alpha"][0, ::2, 1] = 1e-30
+    x["alpha"][0, :, 2] = 50.0
+    x["beta"][0, :, 3] = 0.0
+    S, o = gpu_decode(x)
+    S_ref, o_ref = oracle_decode(x)
+    check_state(f64(S), S_ref, torch.bfloat16)
+    check_o(f64(o), o_ref, torch.bfloat16)
+    y = synth.decode_inputs(2, 3, 64, 5, state_dtype="bf16", seed=121)
+    y["state"][1, 2, 17, 5] = float("nan")
+    S, o = gpu_decode(y)
+    S, o = S.cpu().float(), o.cpu().float()
+    assert torch.isnan(S[1, 2]).any(dim=1).nonzero().flatten().tolist() == [17]
+    assert torch.isnan(o[1, :, 2]).any(dim=0).nonzero().flatten().tolist() == [17]
+    mask = torch.ones(2, 3, dtype=torch.bool)
+    mask[1, 2] = False
+    assert not torch.isnan(S[mask]).any() and not torch.isnan(o.permute(0, 2, 1, 3)[mask]).any()
+
+
 # ------------------------------------------------------------------ invariants
 
 
