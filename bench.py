@@ -96,6 +96,8 @@ def parse_args(argv=None):
     ap.add_argument("--layers", type=int, default=0, help="layer buffers rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
+    ap.add_argument("--cpu-threads", type=int, default=1,
+                    help="host threads for the oracle sample (sequences split over a pool)")
     ap.add_argument("--graph-groups", type=int, default=7, help="graph-replay groups (0 = skip)")
     ap.add_argument("--graph-replays", type=int, default=400, help="launches per graph replay")
     ap.add_argument("--sequential", action="store_true",
@@ -288,28 +290,40 @@ def time_copy(args, mb: int):
 # ----------------------------------------------------------------------------- CPU baseline
 
 
-def cpu_baseline(spec: dict, workload: str, state_dtype: str, target_s: float):
+def cpu_baseline(spec: dict, workload: str, state_dtype: str, target_s: float, threads: int = 1):
     """The fp64 oracle, untuned, on a bounded sample: the first few sequences of the same
-    workload (all heads), repeated until about `target_s` seconds; scaled to one layer."""
-    import numpy as np
+    workload (all heads), repeated until about `target_s` seconds; scaled to one layer. With
+    threads > 1 the sample's sequences are split over a thread pool (the C oracle runs outside
+    the GIL), one oracle call per sequence."""
+    from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     from gated_deltanet_recurrent_02_amd import synth
 
     B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
-    Bs = max(1, min(B, 8))
+    Bs = max(1, min(B, max(8, threads)))
+    threads = max(1, min(threads, Bs))  # one sequence per call: no more threads than sequences
     Ts = T
     if spec.get("prefill"):  # the oracle's time is linear in T: a prefix of one prompt
         Bs, Ts = 1, min(T, 256)
     x = synth.workload_inputs(workload, state_dtype=state_dtype, B=Bs, T=Ts)
     f = lambda t: t.double().numpy()
     if spec.get("fused"):
-        args = (f(x["qkv"]), f(x["conv_state"]), f(x["conv_w"]), None, f(x["a_logit"]),
-                f(x["b_logit"]), f(x["state"]))
-        run = lambda: oracle.gdn_conv_gate_decode(*args, H=H, dk=D, dv=D)
+        names = ("qkv", "conv_state", "a_logit", "b_logit", "state")
+        full = {n: f(x[n]) for n in names}
+        w = f(x["conv_w"])
+        one = lambda sl: oracle.gdn_conv_gate_decode(
+            full["qkv"][sl], full["conv_state"][sl], w, None, full["a_logit"][sl],
+            full["b_logit"][sl], full["state"][sl], H=H, dk=D, dv=D)
     else:
-        args = tuple(f(x[n]) for n in ("q", "k", "v", "alpha", "beta", "state"))
-        run = lambda: oracle.gdn_decode(*args)
+        names = ("q", "k", "v", "alpha", "beta", "state")
+        full = {n: f(x[n]) for n in names}
+        one = lambda sl: oracle.gdn_decode(*(full[n][sl] for n in names))
+    if threads == 1:
+        run = lambda: one(slice(0, Bs))
+    else:
+        pool = ThreadPoolExecutor(threads)
+        run = lambda: list(pool.map(one, [slice(b, b + 1) for b in range(Bs)]))
     oracle.load()
     run()
     reps, t0 = 0, time.perf_counter()
@@ -322,9 +336,10 @@ def cpu_baseline(spec: dict, workload: str, state_dtype: str, target_s: float):
     per_rep = el / reps
     us_per_layer = per_rep * (B / Bs) * (T / Ts) * 1e6
     scaled = f"{B}/{Bs}" + (f" x {T}/{Ts} tokens" if Ts != T else "")
-    return {"value": us_per_layer, "unit": "us/layer", "cores": 1, "kind": "oracle",
+    how = "single-thread" if threads == 1 else f"{threads} threads (one sequence per call)"
+    return {"value": us_per_layer, "unit": "us/layer", "cores": threads, "kind": "oracle",
             "sample": f"{Bs} of {B} sequences x {H} heads (D={D}, T={Ts} of {T}), fp64 "
-                      f"single-thread C oracle, {reps} repetitions in {el:.1f} s, scaled by {scaled}",
+                      f"{how} C oracle, {reps} repetitions in {el:.1f} s, scaled by {scaled}",
             "host_cpus": os.cpu_count()}
 
 
@@ -396,7 +411,8 @@ def main(argv=None):
                             "timed": "whole gdn_prefill call (prep + state kernels)"}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(spec, args.workload, args.state_dtype, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(spec, args.workload, args.state_dtype, args.cpu_seconds,
+                                            args.cpu_threads)
     print(json.dumps(line), flush=True)
     return 0
 
