@@ -542,11 +542,15 @@ __global__ __launch_bounds__(64) void gdn_prefill_state_kernel(
     const int h = (int)(bh % H);
     const int row0 = 16 * RT * wt + n;
 
+    // State rows: each lane reads its D/4 contiguous columns, so one load instruction touches
+    // 16 bytes of each of 64 lines and the lines fill over the run's instructions. Ordinary
+    // (cached) loads and stores let the L2 merge those partial lines; with the nontemporal
+    // hint a short-prompt call (B=256, T=16, fp32 state) took 1159 instead of 534 us.
     f32x4 S[RT][NMT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         Run<ST, R> sr;
-        sr.template load<true>(state + ((size_t)bh * D + row0 + 16 * r) * D + R * g);
+        sr.template load<false>(state + ((size_t)bh * D + row0 + 16 * r) * D + R * g);
 #pragma unroll
         for (int e = 0; e < R; ++e) S[r][e % NMT][e / NMT] = sr.get(e);
     }
@@ -573,7 +577,7 @@ __global__ __launch_bounds__(64) void gdn_prefill_state_kernel(
         float out[R];
 #pragma unroll
         for (int e = 0; e < R; ++e) out[e] = S[r][e % NMT][e / NMT] * cs;
-        store_run<ST, R, true>(state + ((size_t)bh * D + row0 + 16 * r) * D + R * g, out);
+        store_run<ST, R, false>(state + ((size_t)bh * D + row0 + 16 * r) * D + R * g, out);
     }
 }
 

@@ -194,8 +194,8 @@ gdn_status gdn_prefill_workspace_size(int64_t B, int32_t T, int32_t H, int32_t d
  *   workspace_bytes  its size in bytes
  * Errors: as gdn_decode_step; GDN_ERR_INVALID_ARGUMENT also for a workspace smaller than
  * required; GDN_ERR_UNSUPPORTED when B * H * ceil(T / 16) * 64 >= 2^32 (the prep kernel's
- * single dispatch). For runs of up to 16 tokens gdn_decode_step is faster (up to 32 with fp32
- * states at B * H >= 1536); this call always runs the chunked form.
+ * single dispatch). For runs of fewer than 16 tokens gdn_decode_step is faster; this call
+ * always runs the chunked form.
  */
 gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                        const void* q, const void* k, const void* v, gdn_dtype act_dtype,
