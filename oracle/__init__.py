@@ -5,7 +5,8 @@ CPU-baseline leg are the only callers. The product library never imports this pa
 
 The wrapper only marshals numpy arrays (float64, C-contiguous) into the C entry points; every
 step of the arithmetic is in ``gdn_oracle.c``. See that file for the definitions and their
-sources ("GDN tuning limits on Kunlun XPU", section 二 背景).
+sources ("GDN tuning limits on Kunlun XPU", section 二 背景; the sliding-window low-rank state,
+section 三.3).
 """
 from __future__ import annotations
 
@@ -56,6 +57,9 @@ def _declare(lib):
     lib.oracle_gdn_conv_gate_decode.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P,
                                                 P, P, f64, f64]
     lib.oracle_gdn_conv_gate_decode.restype = ctypes.c_int
+    lib.oracle_gdn_lowrank_decode.argtypes = [i64, i32, i32, i32, i32, i32, P, P, P, P, P,
+                                              P, P, P, P, P, f64]
+    lib.oracle_gdn_lowrank_decode.restype = ctypes.c_int
     return lib
 
 
@@ -122,3 +126,27 @@ def gdn_conv_gate_decode(x, conv_state, conv_w, conv_b, a_logit, b_logit, state,
     if rc != 0:
         raise ValueError("oracle_gdn_conv_gate_decode rejected its arguments")
     return S, o, cs
+
+
+def gdn_lowrank_decode(q, k, v, alpha, beta, U, K, c, pos, scale: float = 1.0, lib=None):
+    """T tokens on the sliding-window low-rank state. Shapes: q,k [B,T,H,dk]; v [B,T,H,dv];
+    alpha,beta [B,T,H]; U [B,H,r,dv]; K [B,H,r,dk]; c [B,H,r]; pos [B,H] (int). Returns
+    (U, K, c, pos, o [B,T,H,dv]) as new arrays (pos int32, the rest float64)."""
+    lib = lib or load()
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    U, K, c = (_f64(a).copy() for a in (U, K, c))
+    P = np.ascontiguousarray(np.asarray(pos, dtype=np.int32)).copy()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    r = U.shape[2]
+    assert k.shape == q.shape and v.shape == (B, T, H, dv)
+    assert alpha.shape == (B, T, H) and beta.shape == (B, T, H)
+    assert U.shape == (B, H, r, dv) and K.shape == (B, H, r, dk) and c.shape == (B, H, r)
+    assert P.shape == (B, H)
+    o = np.zeros((B, T, H, dv), dtype=np.float64)
+    rc = lib.oracle_gdn_lowrank_decode(B, T, H, dk, dv, r, _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _ptr(U), _ptr(K), _ptr(c),
+                                       _ptr(P), _ptr(o), float(scale))
+    if rc != 0:
+        raise ValueError("oracle_gdn_lowrank_decode rejected its arguments")
+    return U, K, c, P, o

@@ -21,6 +21,8 @@
  *    S_t - alpha_t S_{t-1} = beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T.
  *  - The conv/SiLU/L2-norm/gate prologue is the "short conv -> gating" part of the same chain;
  *    its exact forms are readings, listed at each function below.
+ *  - The sliding-window low-rank state (same page, section 三.3) keeps only the last r rank-1
+ *    writes of the same rule; its reading is stated at oracle_gdn_lowrank_decode.
  *
  * Layouts (row-major, last index fastest), all fp64:
  *    q, k   [B][T][H][dk]        v, o   [B][T][H][dv]
@@ -29,6 +31,7 @@
  *    x (mixed q|k|v inputs)  [B][T][C],  C = H*dk + H*dk + H*dv, blocks ordered q, k, v,
  *                                       each block head-major with the head dim fastest
  *    conv_state [B][C][3] (oldest first),   conv_w [C][4],   conv_b [C] (optional)
+ *    low-rank window  U [B][H][r][dv], K [B][H][r][dk], c [B][H][r], pos [B][H] (int32)
  *
  * Every entry point returns 0 on success and -1 if a size is non-positive or a pointer is
  * missing; it never aborts.
@@ -195,4 +198,92 @@ int oracle_gdn_conv_gate_decode(int64_t B, int32_t T, int32_t H, int32_t dk, int
     }
     free(q); free(k); free(v); free(al); free(be);
     return rc;
+}
+
+/* The sliding-window low-rank state of "GDN tuning limits on Kunlun XPU", section 三.3 (the
+ * low-rank recurrent route, r = 16 or 32). The page states that its U/V state is a cache of the
+ * most recent r rank-1 updates, not a low-rank factorisation of the state, and gives no
+ * equations. The reading used here: the state a head stands for is the sum of the last r
+ * update terms of the gated delta rule, each decayed by every gate since it was written,
+ *     S_t = sum over the r most recent tokens i <= t of (alpha_{i+1} ... alpha_t) delta_i k_i^T,
+ * where each token's write delta_t = beta_t (v_t - alpha_t S_{t-1} k_t) is the full rule's
+ * write against that windowed S_{t-1}; a token older than the window is dropped whole. With a
+ * window at least as long as the run and an empty start this is exactly the full recurrence.
+ *
+ * Storage, per (sequence, head): r slots, slot i holding a write vector U_i (dv values), its key
+ * K_i (dk values) and a weight c_i (the decay it has collected since it was written), so that
+ * S = sum_i c_i U_i K_i^T; pos is the slot the next token writes (the oldest one once the window
+ * is full), taken modulo r as an unsigned 32-bit value. An all-zero state is the empty window.
+ *
+ * Per token, written out plainly (S is formed as an explicit dv x dk matrix every time):
+ *   1. S = sum_i c_i U_i K_i^T                       (the state before the token)
+ *   2. delta = beta (v - alpha S k)
+ *   3. every weight is multiplied by alpha           (the decay reaches every stored update)
+ *   4. slot pos becomes (delta, k, 1); pos <- (pos + 1) mod r   (the oldest update leaves)
+ *   5. S = sum_i c_i U_i K_i^T again; o = S (scale q)  (the readout uses the updated state)
+ *
+ * Layouts: U [B][H][r][dv], K [B][H][r][dk], c [B][H][r] (fp64), pos [B][H] (int32); q, k, v, o,
+ * alpha, beta as in oracle_gdn_decode. U, K, c and pos are updated in place. */
+static void lowrank_form_state(int32_t r, int32_t dk, int32_t dv, const double* U,
+                               const double* K, const double* c, double* S)
+{
+    for (int32_t i = 0; i < dv; ++i)
+        for (int32_t j = 0; j < dk; ++j) S[(size_t)i * dk + j] = 0.0;
+    for (int32_t s = 0; s < r; ++s)
+        for (int32_t i = 0; i < dv; ++i)
+            for (int32_t j = 0; j < dk; ++j)
+                S[(size_t)i * dk + j] += c[s] * U[(size_t)s * dv + i] * K[(size_t)s * dk + j];
+}
+
+int oracle_gdn_lowrank_decode(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t r,
+                              const double* q, const double* k, const double* v,
+                              const double* alpha, const double* beta,
+                              double* U, double* K, double* c, int32_t* pos,
+                              double* o, double scale)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0 || r <= 0) return -1;
+    if (!q || !k || !v || !alpha || !beta || !U || !K || !c || !pos || !o) return -1;
+    double* S = (double*)malloc(sizeof(double) * (size_t)dv * dk);
+    double* delta = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!S || !delta) { free(S); free(delta); return -1; }
+    for (int64_t b = 0; b < B; ++b) {
+        for (int32_t h = 0; h < H; ++h) {
+            size_t head = (size_t)b * H + h;
+            double* Uh = U + head * (size_t)r * dv;
+            double* Kh = K + head * (size_t)r * dk;
+            double* ch = c + head * (size_t)r;
+            int32_t p = (int32_t)((uint32_t)pos[head] % (uint32_t)r);
+            for (int32_t t = 0; t < T; ++t) {
+                size_t g = ((size_t)b * T + t) * H + h; /* (b, t, h) */
+                const double* kt = k + g * dk;
+                const double* qt = q + g * dk;
+                const double* vt = v + g * dv;
+                /* 1-2: the write against the state before the token */
+                lowrank_form_state(r, dk, dv, Uh, Kh, ch, S);
+                for (int32_t i = 0; i < dv; ++i) {
+                    double acc = 0.0;
+                    for (int32_t j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * kt[j];
+                    delta[i] = beta[g] * (vt[i] - alpha[g] * acc);
+                }
+                /* 3: decay every stored update */
+                for (int32_t s = 0; s < r; ++s) ch[s] = alpha[g] * ch[s];
+                /* 4: the oldest slot takes the new update */
+                for (int32_t i = 0; i < dv; ++i) Uh[(size_t)p * dv + i] = delta[i];
+                for (int32_t j = 0; j < dk; ++j) Kh[(size_t)p * dk + j] = kt[j];
+                ch[p] = 1.0;
+                p = (p + 1) % r;
+                /* 5: readout with the updated state */
+                lowrank_form_state(r, dk, dv, Uh, Kh, ch, S);
+                for (int32_t i = 0; i < dv; ++i) {
+                    double acc = 0.0;
+                    for (int32_t j = 0; j < dk; ++j) acc += S[(size_t)i * dk + j] * (scale * qt[j]);
+                    o[g * dv + i] = acc;
+                }
+            }
+            pos[head] = p;
+        }
+    }
+    free(S);
+    free(delta);
+    return 0;
 }

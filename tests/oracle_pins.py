@@ -354,4 +354,163 @@ RECURRENCE_PINS = [pin_golden_worked, pin_closed_form, pin_identity_gate, pin_ze
                    pin_head_independence, pin_linearity, pin_scale]
 PROLOGUE_PINS = [pin_conv_matches_numpy, pin_conv_bias, pin_conv_identity_taps,
                  pin_conv_state_roll, pin_unit_norm, pin_gates, pin_fused_composes]
-ALL_PINS = RECURRENCE_PINS + PROLOGUE_PINS
+# ----------------------------------------------------------------------------- low-rank window
+#
+# "GDN tuning limits on Kunlun XPU", section 三.3: the low-rank route keeps a cache of the
+# most recent r rank-1 updates (not a factorisation of the state). Reading pinned here: the
+# state is the sum of the last r writes of the gated delta rule, each decayed by every gate
+# since it was written; slot i holds (U_i, K_i, c_i) and stands for c_i U_i K_i^T.
+
+
+def lowrank_effective_state(U, K, c):
+    """sum_i c_i U_i K_i^T per (sequence, head): [B,H,dv,dk]."""
+    return np.einsum("bhs,bhsi,bhsj->bhij", c, U, K)
+
+
+def _lowrank_filled(rng, B, H, r, dk, dv):
+    U = rng.standard_normal((B, H, r, dv)) * 0.5
+    K = rng.standard_normal((B, H, r, dk))
+    K /= np.linalg.norm(K, axis=-1, keepdims=True)
+    c = rng.uniform(0.05, 1.0, (B, H, r))
+    pos = rng.integers(0, r, (B, H)).astype(np.int32)
+    return U, K, c, pos
+
+
+def _lowrank_empty(B, H, r, dk, dv, pos=None):
+    pos = np.zeros((B, H), np.int32) if pos is None else pos
+    return np.zeros((B, H, r, dv)), np.zeros((B, H, r, dk)), np.zeros((B, H, r)), pos
+
+
+def pin_lowrank_long_window_is_full_rank(lib, seed=20):
+    """A window at least as long as the run, from an empty start, is the full recurrence:
+    the same o and the same state as oracle_gdn_decode from S0 = 0 (itself pinned above)."""
+    rng = np.random.default_rng(seed)
+    for r, T in ((8, 5), (8, 8), (12, 7), (3, 3)):
+        q, k, v, al, be, _ = _rand_inputs(rng, 2, T, 3, 8, 8)
+        pos0 = rng.integers(0, r, (2, 3)).astype(np.int32)
+        U, K, c, pos = _lowrank_empty(2, 3, r, 8, 8, pos0)
+        U, K, c, pos, o = oracle.gdn_lowrank_decode(q, k, v, al, be, U, K, c, pos, lib=lib)
+        S_full, o_full = oracle.gdn_decode(q, k, v, al, be, np.zeros((2, 3, 8, 8)), lib=lib)
+        assert np.max(np.abs(o - o_full)) <= 1e-12 * max(1.0, np.max(np.abs(o_full))), (r, T)
+        S = lowrank_effective_state(U, K, c)
+        assert np.max(np.abs(S - S_full)) <= 1e-12 * max(1.0, np.max(np.abs(S_full))), (r, T)
+        assert np.array_equal(pos, (pos0 + T) % r), (r, T)
+
+
+def pin_lowrank_orthogonal_keys(lib, seed=21):
+    """Keys e_0, e_1, ... (mutually orthogonal): no write sees an earlier one, so delta_t =
+    beta_t v_t, and after token t the state's column i is (alpha_{i+1}..alpha_t) beta_i v_i
+    for the r most recent tokens i and exactly zero for every older one."""
+    rng = np.random.default_rng(seed)
+    B, H, D, r, T = 1, 2, 16, 4, 11
+    q, _, v, al, be, _ = _rand_inputs(rng, B, T, H, D, D)
+    k = np.zeros((B, T, H, D))
+    for t in range(T):
+        k[:, t, :, t] = 1.0
+    U, K, c, pos = _lowrank_empty(B, H, r, D, D, np.array([[1, 3]], np.int32))
+    U, K, c, pos, o = oracle.gdn_lowrank_decode(q, k, v, al, be, U, K, c, pos, scale=0.5, lib=lib)
+    for h in range(H):
+        for t in range(T):
+            St = np.zeros((D, D))
+            for i in range(max(0, t - r + 1), t + 1):
+                St[:, i] = np.prod(al[0, i + 1: t + 1, h]) * be[0, i, h] * v[0, i, h]
+            assert np.max(np.abs(o[0, t, h] - St @ (0.5 * q[0, t, h]))) <= 1e-13, (h, t)
+        S = lowrank_effective_state(U, K, c)[0, h]
+        assert np.max(np.abs(S - St)) <= 1e-14, h
+        assert np.all(S[:, : T - r] == 0.0), h
+
+
+def pin_lowrank_single_slot(lib, seed=22):
+    """r = 1 keeps only the newest write: S_t = delta_t k_t^T with
+    delta_t = beta_t (v_t - alpha_t (k_{t-1} . k_t) delta_{t-1}), and o_t = delta_t (k_t . q_t)."""
+    rng = np.random.default_rng(seed)
+    B, H, D, T = 1, 2, 8, 6
+    q, k, v, al, be, _ = _rand_inputs(rng, B, T, H, D, D)
+    U, K, c, pos = _lowrank_empty(B, H, 1, D, D)
+    U, K, c, pos, o = oracle.gdn_lowrank_decode(q, k, v, al, be, U, K, c, pos, lib=lib)
+    for h in range(H):
+        d_prev, k_prev = np.zeros(D), np.zeros(D)
+        for t in range(T):
+            kt = k[0, t, h]
+            d = be[0, t, h] * (v[0, t, h] - al[0, t, h] * np.dot(k_prev, kt) * d_prev)
+            assert np.max(np.abs(o[0, t, h] - d * np.dot(kt, q[0, t, h]))) <= 1e-13, (h, t)
+            d_prev, k_prev = d, kt
+        assert np.max(np.abs(U[0, h, 0] - d_prev)) <= 1e-13 and c[0, h, 0] == 1.0
+
+
+def pin_lowrank_rank_bound(lib, seed=23):
+    """The state is a sum of at most r rank-1 terms: rank <= min(r, tokens seen) although the
+    full recurrence on the same inputs reaches full rank."""
+    rng = np.random.default_rng(seed)
+    B, H, D, r, T = 1, 2, 8, 3, 12
+    q, k, v, al, be, _ = _rand_inputs(rng, B, T, H, D, D)
+    U, K, c, pos = _lowrank_empty(B, H, r, D, D)
+    for t in range(T):
+        sl = slice(t, t + 1)
+        U, K, c, pos, _ = oracle.gdn_lowrank_decode(q[:, sl], k[:, sl], v[:, sl], al[:, sl],
+                                                    be[:, sl], U, K, c, pos, lib=lib)
+        S = lowrank_effective_state(U, K, c)
+        for h in range(H):
+            assert np.linalg.matrix_rank(S[0, h], tol=1e-10) == min(r, t + 1), (t, h)
+    S_full, _ = oracle.gdn_decode(q, k, v, al, be, np.zeros((B, H, D, D)), lib=lib)
+    assert np.linalg.matrix_rank(S_full[0, 0], tol=1e-10) == D
+
+
+def lowrank_window_bruteforce(U, K, c, pos, q, k, v, al, be, scale=1.0):
+    """One head by a different algorithm: the window as a queue of (decayed write, key) pairs,
+    oldest first (slot pos is the oldest), each token appending its write and dropping the
+    oldest, the decay applied to the stored vectors themselves. Returns (S_T, o [T, dv])."""
+    r = U.shape[0]
+    win = [(c[s] * U[s], K[s]) for s in ((pos + j) % r for j in range(r))]
+    outs = []
+    for t in range(len(al)):
+        S = sum(np.outer(w, kk) for w, kk in win)
+        delta = be[t] * (v[t] - al[t] * (S @ k[t]))
+        win = [(al[t] * w, kk) for w, kk in win[1:]] + [(delta, k[t])]
+        S = sum(np.outer(w, kk) for w, kk in win)
+        outs.append(S @ (scale * q[t]))
+    return S, np.array(outs)
+
+
+def pin_lowrank_bruteforce(lib, seed=24):
+    """A filled window (every slot in use, any next slot) against the queue brute force."""
+    rng = np.random.default_rng(seed)
+    B, H, D, r, T = 2, 2, 6, 3, 9
+    q, k, v, al, be, _ = _rand_inputs(rng, B, T, H, D, D)
+    U0, K0, c0, pos0 = _lowrank_filled(rng, B, H, r, D, D)
+    U, K, c, pos, o = oracle.gdn_lowrank_decode(q, k, v, al, be, U0, K0, c0, pos0, scale=0.7,
+                                                lib=lib)
+    S = lowrank_effective_state(U, K, c)
+    for b in range(B):
+        for h in range(H):
+            Sx, ox = lowrank_window_bruteforce(U0[b, h], K0[b, h], c0[b, h], pos0[b, h],
+                                               q[b, :, h], k[b, :, h], v[b, :, h],
+                                               al[b, :, h], be[b, :, h], scale=0.7)
+            assert np.max(np.abs(S[b, h] - Sx)) <= 1e-12 * max(1.0, np.max(np.abs(Sx)))
+            assert np.max(np.abs(o[b, :, h] - ox)) <= 1e-12 * max(1.0, np.max(np.abs(ox)))
+
+
+def pin_lowrank_calls_resume(lib, seed=25):
+    """One call of T tokens equals the same tokens split over several calls, bit for bit."""
+    rng = np.random.default_rng(seed)
+    B, H, D, r, T = 2, 3, 8, 4, 9
+    q, k, v, al, be, _ = _rand_inputs(rng, B, T, H, D, D)
+    st0 = _lowrank_filled(rng, B, H, r, D, D)
+    whole = oracle.gdn_lowrank_decode(q, k, v, al, be, *st0, lib=lib)
+    st, outs = st0, []
+    for a, z in ((0, 4), (4, 5), (5, 9)):
+        sl = slice(a, z)
+        *st, o = oracle.gdn_lowrank_decode(q[:, sl], k[:, sl], v[:, sl], al[:, sl], be[:, sl],
+                                           *st, lib=lib)
+        outs.append(o)
+    for x, y in zip(whole[:4], st):
+        assert np.array_equal(x, y)
+    assert np.array_equal(whole[4], np.concatenate(outs, axis=1))
+
+
+LOWRANK_PINS = [pin_lowrank_long_window_is_full_rank, pin_lowrank_orthogonal_keys,
+                pin_lowrank_single_slot, pin_lowrank_rank_bound, pin_lowrank_bruteforce,
+                pin_lowrank_calls_resume]
+
+ALL_PINS = RECURRENCE_PINS + PROLOGUE_PINS + LOWRANK_PINS
+

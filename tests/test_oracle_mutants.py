@@ -39,6 +39,21 @@ MUTANTS = {
     "alpha_sign": ("alpha[g] = exp(-softplus(a_logit[g]));",
                    "alpha[g] = exp(softplus(a_logit[g]));"),
     "softplus_without_log1p": ("return m + log1p(exp(-fabs(x)));", "return m + exp(-fabs(x));"),
+    "lowrank_old_writes_not_decayed": ("ch[s] = alpha[g] * ch[s];", "ch[s] = ch[s];"),
+    "lowrank_new_write_decayed": ("ch[p] = 1.0;", "ch[p] = alpha[g];"),
+    "lowrank_slot_not_advanced": ("p = (p + 1) % r;", "p = p % r;"),
+    "lowrank_newest_evicted": ("p = (p + 1) % r;", "p = (p + r - 1) % r;"),
+    "lowrank_evict_before_write": ("/* 1-2: the write against the state before the token */",
+                                   "ch[p] = 0.0;"),
+    "lowrank_readout_before_update": (
+        "/* 5: readout with the updated state */\n                lowrank_form_state(r, dk, dv, Uh, Kh, ch, S);",
+        "/* 5 */"),
+    "lowrank_key_from_q": ("Kh[(size_t)p * dk + j] = kt[j];", "Kh[(size_t)p * dk + j] = qt[j];"),
+    "lowrank_write_without_alpha": ("delta[i] = beta[g] * (vt[i] - alpha[g] * acc);",
+                                    "delta[i] = beta[g] * (vt[i] - acc);"),
+    "lowrank_form_transposed_key": (
+        "S[(size_t)i * dk + j] += c[s] * U[(size_t)s * dv + i] * K[(size_t)s * dk + j];",
+        "S[(size_t)i * dk + j] += c[s] * U[(size_t)s * dv + i] * K[(size_t)s * dk + (dk - 1 - j)];"),
 }
 
 
