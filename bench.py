@@ -46,6 +46,8 @@ _CSRC = os.path.join(ROOT, "gated_deltanet_recurrent_02_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_kernels.hip", "gdn_launch.h")]
 PREFILL_SOURCES = [os.path.join(_CSRC, f)
                    for f in ("gdn_prefill.hip", "gdn_prefill_launch.h", "gdn_launch.h")]
+LOWRANK_SOURCES = [os.path.join(_CSRC, f)
+                   for f in ("gdn_lowrank.hip", "gdn_lowrank_launch.h", "gdn_launch.h")]
 
 
 def code_text(src: str) -> str:
@@ -74,12 +76,12 @@ def code_text(src: str) -> str:
     return " ".join("".join(out).split())
 
 
-def kernel_source_hash(prefill: bool = False) -> str:
-    """Hash of the code a workload runs: the kernel sources (decode kernels or the prefill
-    kernels) as code_text, plus the compiler flags they are built with."""
+def kernel_source_hash(prefill: bool = False, lowrank: bool = False) -> str:
+    """Hash of the code a workload runs: the kernel sources (decode, prefill or low-rank
+    window kernels) as code_text, plus the compiler flags they are built with."""
     from gated_deltanet_recurrent_02_amd import build as gdn_build
     h = hashlib.sha256()
-    for p in (PREFILL_SOURCES if prefill else KERNEL_SOURCES):
+    for p in (PREFILL_SOURCES if prefill else LOWRANK_SOURCES if lowrank else KERNEL_SOURCES):
         with open(p, encoding="utf-8") as f:
             h.update(code_text(f.read()).encode())
     h.update(" ".join(gdn_build.HIPFLAGS).encode())
@@ -112,6 +114,13 @@ def algorithmic_bytes(spec: dict, state_dtype: str) -> int:
     """Bytes the step must move once: state read + written, per-token vectors, outputs."""
     B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
     sb = 4 if state_dtype == "f32" else 2
+    if spec.get("lowrank"):
+        # the window read once (U, K, weights, pos); the slots written (one per token, at most
+        # r), every weight and pos written back; the per-token vectors and o
+        r, ab = spec["r"], 4 if spec["act"] == "f32" else 2
+        read = B * H * (2 * r * D * sb + 4 * r + 4)
+        write = B * H * (min(T, r) * 2 * D * sb + 4 * r + 4)
+        return read + write + B * T * H * (3 * D * ab + 8 + D * ab)
     state = 2 * B * H * D * D * sb
     if spec.get("verify"):
         from gated_deltanet_recurrent_02_amd import synth
@@ -132,12 +141,15 @@ def algorithmic_bytes(spec: dict, state_dtype: str) -> int:
 
 
 def flops(spec: dict) -> int:
-    """Arithmetic of the recurrence: u = S k, S q (2 x 2D^2), update (2D^2), k.q, delta, o."""
+    """Arithmetic of the recurrence: u = S k, S q (2 x 2D^2), update (2D^2), k.q, delta, o.
+    On the low-rank window: K k, K q (2 x 2rD), k.q, the two sums over slots (2 x 2rD)."""
     B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
+    if spec.get("lowrank"):
+        return B * H * T * (8 * spec["r"] * D + 6 * D)
     return B * H * T * (6 * D * D + 6 * D)
 
 
-def read_traffic(workload: str, state_dtype: str, prefill: bool = False):
+def read_traffic(workload: str, state_dtype: str, prefill: bool = False, lowrank: bool = False):
     """Measured HBM bytes per launch from profiles/traffic_<workload>_<state>.txt, if the
     kernel source still hashes to the value recorded there; else None."""
     path = os.path.join(PROFILES, f"traffic_{workload}_{state_dtype}.txt")
@@ -149,7 +161,7 @@ def read_traffic(workload: str, state_dtype: str, prefill: bool = False):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash(prefill):
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(prefill, lowrank):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -169,9 +181,11 @@ def time_gpu(args, spec, workload):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fused = spec.get("fused", False)
+    lowrank = spec.get("lowrank", False)
+    state_keys = ("U", "K", "c", "pos") if lowrank else ("state",)
     x = synth.workload_inputs(workload, state_dtype=args.state_dtype)
     x_B, x_T = x["B"], x["T"]
-    state_bytes = x["state"].numel() * x["state"].element_size()
+    state_bytes = sum(x[n].numel() * x[n].element_size() for n in state_keys)
     layer_bytes = sum(v.numel() * v.element_size() for v in x.values() if isinstance(v, torch.Tensor))
     L = args.layers or max(1, math.ceil(2 * MALL_BYTES / layer_bytes))
     L = min(L, 64)
@@ -181,7 +195,8 @@ def time_gpu(args, spec, workload):
     for i in range(L):
         g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
         if i > 0:  # every layer has its own state; copies of the same draw are enough
-            g["state"] = g["state"].clone()
+            for n in state_keys:
+                g[n] = g[n].clone()
         if fused:
             g["o"] = torch.empty((x["B"], x["T"], x["H"], x["D"]), dtype=torch.bfloat16, device=dev)
         else:
@@ -208,6 +223,10 @@ def time_gpu(args, spec, workload):
         def step(g):
             gdn.prefill(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state"], o=g["o"],
                         workspace=ws)
+    elif lowrank:
+        def step(g):
+            gdn.lowrank_decode_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["U"], g["K"],
+                                    g["c"], g["pos"], o=g["o"])
     elif fused:
         def step(g):
             gdn.conv_gate_decode(g["qkv"], g["conv_state"], g["conv_w"], g["conv_b"], g["a_logit"],
@@ -251,7 +270,7 @@ def time_gpu(args, spec, workload):
         extra["graph_protocol"] = f"median of {args.graph_groups} graph replays x {args.graph_replays} launches"
         del g
     # Plain device copy of the same number of state bytes: the read+write ceiling of this machine.
-    src = layers[0]["state"]
+    src = layers[0][state_keys[0]]
     dst = torch.empty_like(src)
     for _ in range(5):
         dst.copy_(src)
@@ -308,7 +327,12 @@ def cpu_baseline(spec: dict, workload: str, state_dtype: str, target_s: float, t
         Bs, Ts = 1, min(T, 256)
     x = synth.workload_inputs(workload, state_dtype=state_dtype, B=Bs, T=Ts)
     f = lambda t: t.double().numpy()
-    if spec.get("fused"):
+    if spec.get("lowrank"):
+        names = ("q", "k", "v", "alpha", "beta", "U", "K", "c")
+        full = {n: f(x[n]) for n in names}
+        full["pos"] = x["pos"].numpy()
+        one = lambda sl: oracle.gdn_lowrank_decode(*(full[n][sl] for n in names + ("pos",)))
+    elif spec.get("fused"):
         names = ("qkv", "conv_state", "a_logit", "b_logit", "state")
         full = {n: f(x[n]) for n in names}
         w = f(x["conv_w"])
@@ -368,6 +392,7 @@ def main(argv=None):
     from gated_deltanet_recurrent_02_amd import synth
     spec = dict(synth.WORKLOADS[args.workload])
     chunked = bool(spec.get("prefill")) and not args.sequential
+    lowrank = bool(spec.get("lowrank"))
     ms, L, extra = time_gpu(args, spec, args.workload)
     us = ms * 1e3
     nbytes = algorithmic_bytes(spec, args.state_dtype)
@@ -382,18 +407,19 @@ def main(argv=None):
         "config": {"workload": args.workload, "B": B, "H": H, "dk": D, "dv": D, "T": T,
                    "state_dtype": args.state_dtype, "act_dtype": act,
                    "entry_point": ("gdn_conv_gate_decode" if spec.get("fused") else
+                                   "gdn_lowrank_decode_step" if lowrank else
                                    "gdn_decode_verify" if spec.get("verify") else
                                    "gdn_prefill" if spec.get("prefill") and not args.sequential else
                                    "gdn_decode_step"),
-                   "layers_rotated": L},
+                   "layers_rotated": L, **({"r": spec["r"]} if lowrank else {})},
         "achieved_gbps": gbps,
         "seq_tokens_per_s": B * T / (ms * 1e-3),
         "us_per_token_48_layers": us * 48,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": gbps / PEAK_HBM_GBPS,
-                     "traffic": read_traffic(args.workload, args.state_dtype, chunked),
+                     "traffic": read_traffic(args.workload, args.state_dtype, chunked, lowrank),
                      "algorithmic_bytes_per_launch": nbytes,
-                     "kernel_source_sha256_16": kernel_source_hash(chunked)},
+                     "kernel_source_sha256_16": kernel_source_hash(chunked, lowrank)},
         "gflops": flops(spec) / (ms * 1e-3) / 1e9,
     }
     line.update(extra)

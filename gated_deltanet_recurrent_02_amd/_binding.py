@@ -22,7 +22,7 @@ _CODE_DTYPE = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16, GDN_F16: torch.
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_state_alloc", "gdn_state_free", "gdn_decode_step", "gdn_decode_verify",
            "gdn_conv_gate_decode", "gdn_prefill_workspace_size", "gdn_prefill",
-           "gdn_status_string", "gdn_last_error")
+           "gdn_lowrank_decode_step", "gdn_status_string", "gdn_last_error")
 
 
 class GDNError(RuntimeError):
@@ -66,6 +66,9 @@ def _declare(L):
     L.gdn_prefill.argtypes = [i64, i32, i32, i32, i32, P, P, P, i, P, P, P, i, P, f32, P,
                               ctypes.c_size_t, P]
     L.gdn_prefill.restype = i
+    L.gdn_lowrank_decode_step.argtypes = [i64, i32, i32, i32, i32, i32, P, P, P, i, P, P, P, P, i,
+                                          P, P, P, f32, P]
+    L.gdn_lowrank_decode_step.restype = i
     L.gdn_status_string.argtypes = [i]
     L.gdn_status_string.restype = ctypes.c_char_p
     L.gdn_last_error.argtypes = []
@@ -233,6 +236,45 @@ def conv_gate_decode(qkv, conv_state, conv_w, conv_b, a_logit, b_logit, state, o
                                      _ptr(conv_b), _ptr(a_logit), _ptr(b_logit), _ptr(state),
                                      _DTYPE_CODE[state.dtype], _ptr(o), float(scale),
                                      float(l2_eps), _stream(qkv.device)))
+    return o
+
+
+def lowrank_state(B: int, H: int, r: int, dk: int, dv: int, dtype: torch.dtype = torch.float32,
+                  device="cuda") -> dict:
+    """An empty sliding window (every slot zero, next slot 0) for lowrank_decode_step:
+    U [B,H,r,dv] and K [B,H,r,dk] of `dtype`, c fp32 [B,H,r], pos int32 [B,H]."""
+    return dict(U=torch.zeros((B, H, r, dv), dtype=dtype, device=device),
+                K=torch.zeros((B, H, r, dk), dtype=dtype, device=device),
+                c=torch.zeros((B, H, r), dtype=torch.float32, device=device),
+                pos=torch.zeros((B, H), dtype=torch.int32, device=device))
+
+
+def lowrank_decode_step(q, k, v, alpha, beta, U, K, c, pos, o=None, scale: float = 1.0):
+    """gdn_lowrank_decode_step on torch tensors: T tokens on a sliding window of the last r
+    writes; updates U, K, c and pos in place and returns o.
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (fp32, bf16 or fp16); alpha, beta fp32 [B,T,H];
+    U [B,H,r,dv] and K [B,H,r,dk] in one state dtype (fp32, bf16 or fp16); c fp32 [B,H,r];
+    pos int32 [B,H]; o (optional) [B,T,H,dv] in the activation dtype."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    r = U.shape[2] if U.dim() == 4 else -1
+    _need(q, "q", (B, T, H, dk), _ACT)
+    _need(k, "k", (B, T, H, dk), (q.dtype,))
+    _need(v, "v", (B, T, H, dv), (q.dtype,))
+    _need(alpha, "alpha", (B, T, H), (torch.float32,))
+    _need(beta, "beta", (B, T, H), (torch.float32,))
+    _need(U, "U", (B, H, r, dv), _ACT)
+    _need(K, "K", (B, H, r, dk), (U.dtype,))
+    _need(c, "c", (B, H, r), (torch.float32,))
+    _need(pos, "pos", (B, H), (torch.int32,))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    _need(o, "o", (B, T, H, dv), (q.dtype,))
+    check(lib().gdn_lowrank_decode_step(B, T, H, dk, dv, r, _ptr(q), _ptr(k), _ptr(v),
+                                        _DTYPE_CODE[q.dtype], _ptr(alpha), _ptr(beta), _ptr(U),
+                                        _ptr(K), _DTYPE_CODE[U.dtype], _ptr(c), _ptr(pos),
+                                        _ptr(o), float(scale), _stream(q.device)))
     return o
 
 

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgdn.so")
 SOURCES = [os.path.join(CSRC, "gdn_kernels.hip"), os.path.join(CSRC, "gdn_prefill.hip"),
-           os.path.join(CSRC, "gdn_api.cpp")]
+           os.path.join(CSRC, "gdn_lowrank.hip"), os.path.join(CSRC, "gdn_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -11,6 +11,7 @@
 #include <string>
 
 #include "gdn_launch.h"
+#include "gdn_lowrank_launch.h"
 #include "gdn_prefill_launch.h"
 
 namespace {
@@ -365,6 +366,56 @@ gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
     a.ws = static_cast<float*>(workspace);
     hipError_t e = gdn::launch_prefill(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip("gdn_prefill: kernel launch", e);
+    return GDN_OK;
+}
+
+gdn_status gdn_lowrank_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                   int32_t r, const void* q, const void* k, const void* v,
+                                   gdn_dtype act_dtype, const float* alpha, const float* beta,
+                                   void* U, void* K, gdn_dtype state_dtype, float* c,
+                                   int32_t* pos, void* o, float scale, void* stream) {
+    static const char* fn = "gdn_lowrank_decode_step";
+    g_last_error.clear();
+    gdn_status s = check_shape(fn, B, T, H, dk, dv);
+    if (s != GDN_OK) return s;
+    if (!valid_dtype(act_dtype) || !valid_dtype(state_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": bad dtype");
+    if (r < 1) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": r must be >= 1");
+    if (!gdn::lowrank_supported_r(r))
+        return fail(GDN_ERR_UNSUPPORTED, std::string(fn) + ": supported windows are r in {8, 16, 32}, got " +
+                                             std::to_string(r));
+    if (B == 0 || T == 0) return GDN_OK;
+    s = check_ptrs(fn, {{"q", q}, {"k", k}, {"v", v}, {"alpha", alpha}, {"beta", beta},
+                        {"U", U}, {"K", K}, {"c", c}, {"pos", pos}, {"o", o}});
+    if (s != GDN_OK) return s;
+    const size_t tokens = (size_t)B * T * H;
+    const size_t heads = (size_t)B * H;
+    const size_t ab = dtype_bytes(act_dtype), sb = dtype_bytes(state_dtype);
+    const Range r_q = range("q", q, tokens * dk * ab), r_k = range("k", k, tokens * dk * ab);
+    const Range r_v = range("v", v, tokens * dv * ab), r_a = range("alpha", alpha, tokens * 4);
+    const Range r_b = range("beta", beta, tokens * 4), r_o = range("o", o, tokens * dv * ab);
+    const Range r_U = range("U", U, heads * r * dv * sb), r_K = range("K", K, heads * r * dk * sb);
+    const Range r_c = range("c", c, heads * r * 4), r_p = range("pos", pos, heads * 4);
+    s = check_disjoint(fn, r_o, {r_q, r_k, r_v, r_a, r_b, r_U, r_K, r_c, r_p});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_U, {r_q, r_k, r_v, r_a, r_b, r_K, r_c, r_p});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_K, {r_q, r_k, r_v, r_a, r_b, r_c, r_p});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_c, {r_q, r_k, r_v, r_a, r_b, r_p});
+    if (s != GDN_OK) return s;
+    s = check_disjoint(fn, r_p, {r_q, r_k, r_v, r_a, r_b});
+    if (s != GDN_OK) return s;
+
+    gdn::LowrankArgs a;
+    a.B = B; a.T = T; a.H = H; a.D = dk; a.R = r;
+    a.q = q; a.k = k; a.v = v; a.act = to_dtype(act_dtype);
+    a.alpha = alpha; a.beta = beta;
+    a.U = U; a.K = K; a.state_dtype = to_dtype(state_dtype);
+    a.c = c; a.pos = pos;
+    a.o = o; a.scale = scale;
+    hipError_t e = gdn::launch_lowrank(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip("gdn_lowrank_decode_step: kernel launch", e);
     return GDN_OK;
 }
 

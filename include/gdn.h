@@ -204,6 +204,42 @@ gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                        void* o, float scale, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * gdn_lowrank_decode_step — T tokens of the recurrence on a sliding-window low-rank state, the
+ * low-rank route of "GDN tuning limits on Kunlun XPU", section 三.3 (r = 16 or 32 there). That
+ * page states that this state caches the most recent r rank-1 updates and is not a
+ * factorisation of the full state; it prints no equations. Reading implemented: the state a
+ * head stands for is the sum of the last r writes of the gated delta rule above, each decayed
+ * by every gate since it was written, and each write is the full rule's write against that
+ * windowed state. With r >= the tokens seen since an empty start this is exactly
+ * gdn_decode_step; afterwards the oldest write leaves the window whole.
+ *
+ * Storage per (b, h): r slots; slot i holds a write vector U_i, its key K_i and a weight c_i,
+ * and the state is S = sum_i c_i U_i K_i^T; pos is the slot the next token writes (the oldest
+ * write once the window is full). Per token:
+ *     delta = beta (v - alpha S k);  every c_i *= alpha;  slot pos <- (delta, k, 1);
+ *     pos <- (pos + 1) mod r;        o = S_new (scale q)
+ * An all-zero window (U, K, c and pos zero) is the empty state of a new sequence.
+ *
+ *   q, k, v, alpha, beta, o, act_dtype, scale   as gdn_decode_step
+ *   r      window length: 8, 16 or 32 (GDN_ERR_UNSUPPORTED otherwise)
+ *   U      state_dtype [B][H][r][dv]  write vectors, updated IN PLACE
+ *   K      state_dtype [B][H][r][dk]  keys, updated IN PLACE (k rounded to state_dtype)
+ *   c      fp32 [B][H][r]             weights, updated IN PLACE
+ *   pos    int32 [B][H]               next slot, read modulo r as an unsigned value and
+ *                                     written back as (pos + T) mod r
+ * Within one call U, K and c stay fp32 in registers; only the slots the call wrote (one per
+ * token, all r once T >= r), every weight and pos are stored. Stores to a 16-bit state round to
+ * nearest even once per call. Non-finite inputs stay within their own (b, h).
+ * Errors: as gdn_decode_step; U, K, c and pos must not overlap each other or the inputs, and o
+ * must not overlap any argument (GDN_ERR_INVALID_ARGUMENT).
+ */
+gdn_status gdn_lowrank_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                                   int32_t r, const void* q, const void* k, const void* v,
+                                   gdn_dtype act_dtype, const float* alpha, const float* beta,
+                                   void* U, void* K, gdn_dtype state_dtype, float* c,
+                                   int32_t* pos, void* o, float scale, void* stream);
+
 /* gdn_status_string — static name of a status code ("GDN_OK", ...; "unknown" otherwise). */
 const char* gdn_status_string(gdn_status s);
 

@@ -114,3 +114,61 @@ def sample_heads(B: int, H: int, n: int, seed: int = 0):
     while len(pairs) < min(n + 2, B * H):
         pairs.add((int(rng.integers(B)), int(rng.integers(H))))
     return sorted(pairs)
+
+
+# ----------------------------------------------------------------------------- low-rank window
+
+LOWRANK_STATE = ("U", "K", "c", "pos")
+TOL_C = 1e-5  # the weights are fp32 products of fp32 gates: a few roundings per token
+
+
+def gpu_lowrank(x: dict, scale: float = 1.0):
+    """gdn_lowrank_decode_step on device copies; returns (device dict with U, K, c, pos
+    updated, o)."""
+    g = to_dev(x)
+    o = gdn.lowrank_decode_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["U"], g["K"],
+                                g["c"], g["pos"], scale=scale)
+    torch.cuda.synchronize()
+    return g, o
+
+
+def oracle_lowrank(x: dict, scale: float = 1.0, heads=None):
+    """The oracle on every head, or on the listed (b, h) pairs one by one. Returns
+    (U, K, c, pos, o) with the sampled heads first when `heads` is given ([n, ...] and o
+    [n, T, dv]), else the full arrays."""
+    if heads is None:
+        return oracle.gdn_lowrank_decode(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["alpha"]),
+                                         f64(x["beta"]), f64(x["U"]), f64(x["K"]), f64(x["c"]),
+                                         x["pos"].numpy(), scale=scale)
+    b, h = np.asarray(heads).T
+    bt, ht = torch.as_tensor(b), torch.as_tensor(h)
+    sel = lambda t: t[bt, :, ht]
+    q, k, v = (f64(sel(x[n]))[:, :, None] for n in ("q", "k", "v"))
+    al, be = (f64(sel(x[n]))[:, :, None] for n in ("alpha", "beta"))
+    U, K, c = (f64(x[n][bt, ht])[:, None] for n in ("U", "K", "c"))
+    pos = x["pos"][bt, ht].numpy()[:, None]
+    U, K, c, pos, o = oracle.gdn_lowrank_decode(q, k, v, al, be, U, K, c, pos, scale=scale)
+    return U[:, 0], K[:, 0], c[:, 0], pos[:, 0], o[:, :, 0]
+
+
+def effective_state(U: np.ndarray, K: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """sum_i c_i U_i K_i^T over the slot axis (third from last of U)."""
+    return np.einsum("...s,...si,...sj->...ij", c, U, K)
+
+
+def check_lowrank(got: dict, o, ref, act: torch.dtype, sdt: torch.dtype):
+    """got: U, K, c, pos (device or host tensors, same leading axes as ref); o [..., T, H, dv]
+    or [n, T, dv]; ref = (U, K, c, pos, o) from the oracle. K is a copy of k rounded to the
+    state dtype: bit-exact; pos: exact; U per head at the state bar; c at TOL_C; o at the
+    activation bar; and the state the window stands for at the state bar."""
+    U_ref, K_ref, c_ref, pos_ref, o_ref = ref
+    U, K, c = (f64(got[n]) for n in ("U", "K", "c"))
+    assert np.array_equal(got["pos"].cpu().numpy(), pos_ref), "pos"
+    K_exp = f64(torch.from_numpy(K_ref).to(sdt))
+    assert np.array_equal(K, K_exp), f"K: {int((K != K_exp).sum())} keys differ from k in {sdt}"
+    e_c = head_rel_err(c, c_ref, 1)
+    assert e_c <= TOL_C, f"c: per-head relative error {e_c:.3e} > {TOL_C}"
+    check_state(U, U_ref, sdt, "U")
+    check_state(effective_state(U, K, c), effective_state(U_ref, K_ref, c_ref), sdt,
+                "effective state")
+    return check_o(f64(o), o_ref, act)

@@ -285,3 +285,57 @@ def test_prefill_empty_work_and_valid_call_without_device():
     assert gdn.lib().gdn_prefill(2, 0, 4, 16, 16, N, N, N, F32, N, N, N, F32, N, 1.0, N, 0, None) == 0
     assert prefill() == HIP
     assert "kernel launch" in last_error()
+
+
+def lowrank(B=2, T=2, H=4, D=16, r=16, q=None, k=None, v=None, act=F32, alpha=None, beta=None,
+            U=None, K=None, sdt=F32, c=None, pos=None, o=None):
+    """gdn_lowrank_decode_step with disjoint fake buffers unless a pointer is given."""
+    L = gdn.lib()
+    q = P(0) if q is None else q
+    k = P(16 * MB) if k is None else k
+    v = P(32 * MB) if v is None else v
+    alpha = P(48 * MB) if alpha is None else alpha
+    beta = P(64 * MB) if beta is None else beta
+    U = P(80 * MB) if U is None else U
+    K = P(100 * MB) if K is None else K
+    c = P(120 * MB) if c is None else c
+    pos = P(130 * MB) if pos is None else pos
+    o = P(160 * MB) if o is None else o
+    return L.gdn_lowrank_decode_step(B, T, H, D, D, r, q, k, v, act, alpha, beta, U, K, sdt, c,
+                                     pos, o, 1.0, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H=0), INVALID, "H must be"),
+    (dict(D=96), UNSUPPORTED, "head dims"),
+    (dict(act=5), INVALID, "dtype"),
+    (dict(r=0), INVALID, "r must be"),
+    (dict(r=12), UNSUPPORTED, "r in {8, 16, 32}"),
+    (dict(r=64), UNSUPPORTED, "r in {8, 16, 32}"),
+    (dict(c=ctypes.c_void_p(0)), INVALID, "c is NULL"),
+    (dict(pos=P(130 * MB + 4)), INVALID, "pos is not 16-byte aligned"),
+    (dict(o=P(100 * MB)), INVALID, "o overlaps K"),
+    (dict(U=P(100 * MB)), INVALID, "U overlaps K"),
+    (dict(K=P(16 * MB)), INVALID, "K overlaps k"),
+    (dict(c=P(130 * MB)), INVALID, "c overlaps pos"),
+    (dict(pos=P(48 * MB)), INVALID, "pos overlaps alpha"),
+    (dict(B=1 << 20, H=1 << 5), UNSUPPORTED, "B * H * 8 * dk"),
+])
+@fake_ptrs
+def test_lowrank_decode_step_rejects(kw, status, msg):
+    assert lowrank(**kw) == status
+    assert msg in last_error()
+
+
+@fake_ptrs
+def test_lowrank_empty_work_and_valid_call_without_device():
+    N = ctypes.c_void_p(0)
+    L = gdn.lib()
+    for B, T in ((0, 1), (3, 0)):
+        assert L.gdn_lowrank_decode_step(B, T, 4, 128, 128, 16, N, N, N, BF16, N, N, N, N, F32, N,
+                                         N, N, 1.0, None) == 0
+    # U holds B*H*r*D fp32 = 2*4*16*16*4 = 8 KiB: K right after it is valid
+    assert lowrank(K=P(80 * MB + 8192)) == HIP
+    assert lowrank(K=P(80 * MB + 8192 - 16)) == INVALID
+    assert lowrank() == HIP
+    assert "kernel launch" in last_error()
