@@ -16,17 +16,11 @@
 // The dv x dk state is never formed: a token costs O(r D) instead of O(D^2) and the HBM
 // traffic is the window read once plus the slots written, the weights and pos.
 //
-// Mapping: one wave64 per head, four heads per workgroup; the wave keeps the whole window in
-// registers for all T tokens of the call:
-//   * keys: slot i lives in lanes [i LPK, (i+1) LPK), LPK = 64 / r, each lane a contiguous
-//     run of EK = D / LPK columns; K_i . k and K_i . q reduce across those lanes with DPP and
-//     lane i LPK's total is read into a scalar register, so every per-slot coefficient is
-//     uniform across the wave (k . q reduces the same way: each key group holds the same
-//     columns of k and q);
-//   * writes: lane l holds EU = D / 64 consecutive columns of every slot's U (for D < 64,
-//     column l mod D; lanes >= D repeat that work and store nothing), so u, delta and o are
-//     lane-local sums over the slots with scalar coefficients;
-//   * weights and pos are uniform across the wave.
+// Mapping (see LrGeo and gdn_lowrank_kernel): at D = 128 two wave64s share a head (four for a
+// 32-slot fp32 window), each holding its share of the key slots and of the write columns
+// (8 KiB of a 16-slot fp32 window), and trade their per-slot key products through LDS once
+// per token; at D = 64 two waves share a head; below, one wave holds a whole head. Every wave
+// keeps its share of the window in registers for all T tokens of the call.
 // Only the slots the call wrote (one per token; all of them once T >= r) are stored back.
 
 #include <hip/hip_runtime.h>
@@ -78,8 +72,9 @@ template <> struct Elt<_Float16> {
 // ------------------------------------------------------------------ vector memory
 
 // N consecutive elements of T at p (aligned to their total size, a power of two) into
-// floats, with the widest accesses that fit (16, 8, 4 or 2 bytes).
-template <typename T, int N>
+// floats, with the widest accesses that fit (16, 8, 4 or 2 bytes); NT marks the loads
+// nontemporal (streamed past the caches' retention).
+template <typename T, int N, bool NT = false>
 __device__ __forceinline__ void load_run(const T* p, float (&x)[N]) {
     constexpr int BYTES = N * (int)sizeof(T);
     if constexpr (BYTES == 2) {
@@ -91,15 +86,16 @@ __device__ __forceinline__ void load_run(const T* p, float (&x)[N]) {
         if constexpr (BYTES % 16 == 0) {
 #pragma unroll
             for (int i = 0; i < W / 4; ++i) {
-                const lr_u32x4 v = ((const lr_u32x4*)p)[i];
+                const lr_u32x4 v = NT ? __builtin_nontemporal_load((const lr_u32x4*)p + i)
+                                      : ((const lr_u32x4*)p)[i];
                 w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
             }
         } else if constexpr (BYTES == 8) {
-            const lr_u32x2 v = *(const lr_u32x2*)p;
+            const lr_u32x2 v = NT ? __builtin_nontemporal_load((const lr_u32x2*)p) : *(const lr_u32x2*)p;
             w[0] = v.x; w[1] = v.y;
         } else {
             static_assert(BYTES == 4, "run size");
-            w[0] = *(const uint32_t*)p;
+            w[0] = NT ? __builtin_nontemporal_load((const uint32_t*)p) : *(const uint32_t*)p;
         }
 #pragma unroll
         for (int e = 0; e < N; ++e) x[e] = Elt<T>::get(w[e / Elt<T>::per_word], e % Elt<T>::per_word);
@@ -148,6 +144,12 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Sum over aligned groups of 16 lanes (one DPP row); every lane of the row gets the total.
+__device__ __forceinline__ float row_sum16(float x) {
+    x = group_sum<8>(x);
+    return x + lr_dpp<0x140>(x);                  // row_mirror: the other half of the row
+}
+
 // A value every lane holds identically, kept in a scalar register.
 __device__ __forceinline__ float uniform_f(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
@@ -159,121 +161,195 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
 
 // ------------------------------------------------------------------ the kernel
 
+// Most waves that share one head at D = 128, chosen by measurement on MI355X (B = 256, H = 48):
+// four for a 32-slot fp32 window (88.5 -> 78.6 us per call against two), two otherwise (four
+// waves lose 2-22% on 16-slot and 16-bit windows and on multi-token calls). The window is
+// read once per call, so its loads are nontemporal (16-slot fp32: 44.7 -> 39.2 us).
+template <int R, typename ST>
+constexpr int lr_max_waves() { return sizeof(ST) == 4 && R >= 32 ? 4 : 2; }
+constexpr bool kLrStateNT = true;
+
+// Geometry of one instance: head dim D, window R, storage types AT (activations), ST (state).
 template <int D, int R, typename AT, typename ST>
-__global__ __launch_bounds__(64 * kLowrankHeadsPerGroup) void gdn_lowrank_kernel(LowrankArgs a) {
-    constexpr int LPK = 64 / R;                 // lanes per key slot
-    constexpr int EK = D / LPK;                 // key columns per lane
-    constexpr int EU = D >= 64 ? D / 64 : 1;    // write columns per lane
-    constexpr int KCH = (16 / (int)sizeof(AT)) < EK ? (16 / (int)sizeof(AT)) : EK;  // per load
-    static_assert(EK % KCH == 0, "key run");
+struct LrGeo {
+    // waves per head: D / 32 (one wave below D = 64), at most lr_max_waves, and few enough that
+    // every wave owns at least 4 key slots
+    static constexpr int W0 = D / 32 < lr_max_waves<R, ST>() ? D / 32 : lr_max_waves<R, ST>();
+    static constexpr int W1 = W0 < R / 4 ? W0 : R / 4;
+    static constexpr int W = W1 < 1 ? 1 : W1;
+    static constexpr int RW = R / W;                      // key slots per wave
+    static constexpr int LPK = 64 / RW;                   // lanes per key slot
+    static constexpr int EK = D / LPK;                    // key columns per lane
+    static constexpr int CHE = (16 / (int)sizeof(ST)) < EK ? (16 / (int)sizeof(ST)) : EK;
+    static constexpr int NCH = EK / CHE;                  // key chunks per lane
+    static constexpr int DW = D / W;                      // write columns per wave
+    static constexpr int SG = 64 / DW;                    // lanes per write column
+    static constexpr int RS = R / SG;                     // write slots per lane
+    static_assert(LPK >= 2 && LPK <= 16 && EK * LPK == D && NCH * CHE == EK, "key layout");
+    static_assert(DW <= 64 && SG * DW == 64 && (SG == 1 || SG == 2 || SG == 4) && RS >= 1,
+                  "write layout");
+};
+
+template <int G>
+__device__ __forceinline__ float slot_sum(float x) {
+    if constexpr (G == 16) return row_sum16(x);
+    else return group_sum<G>(x);
+}
+
+// Sum over the SG lanes that hold one write column (lanes l, l ^ DW, ...).
+template <int SG, int DW>
+__device__ __forceinline__ float column_sum(float x) {
+    if constexpr (SG >= 2) x += __shfl_xor(x, DW, 64);
+    if constexpr (SG == 4) x += __shfl_xor(x, 2 * DW, 64);
+    return x;
+}
+
+// W wave64s per (sequence, head); every wave keeps its share of the window in registers for
+// all T tokens of the call:
+//   * keys: the wave owns slots [w RW, (w+1) RW); slot i lives in LPK lanes, lane j of them
+//     holding the 16-byte column chunks j, j + LPK, j + 2 LPK, ... (one load instruction covers
+//     LPK * 16 contiguous bytes of each of RW rows). K_i . k and K_i . q reduce across the
+//     slot's lanes with DPP, and the slot totals go through LDS (one barrier per token) to
+//     the lanes that hold that slot's writes;
+//   * writes: the wave owns columns [w DW, (w+1) DW) of every slot's U; lane l holds column
+//     w DW + l mod DW of the RS slots of its slot group l / DW, with those slots' weights, so
+//     u, y, delta and o are lane-local sums over slots plus one cross-lane sum over the SG
+//     groups of a column;
+//   * pos is uniform across the workgroup; wave 0 stores the weights and pos.
+// One head per workgroup.
+template <int D, int R, typename AT, typename ST>
+__global__ __launch_bounds__((64 * LrGeo<D, R, AT, ST>::W))
+void gdn_lowrank_kernel(LowrankArgs a) {
+    using G = LrGeo<D, R, AT, ST>;
+    constexpr int W = G::W, RW = G::RW, LPK = G::LPK, EK = G::EK, CHE = G::CHE, NCH = G::NCH;
+    constexpr int DW = G::DW, SG = G::SG, RS = G::RS;
+    __shared__ float xchg[2][2][R];   // [token parity][K.k, K.q][slot]
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t head = (int64_t)blockIdx.x * kLowrankHeadsPerGroup + wave;  // b * H + h
-    if (head >= a.B * a.H) return;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave within the head
+    const int64_t head = blockIdx.x;                                   // b * H + h
     const int64_t b = head / a.H;
     const int h = (int)(head - b * a.H);
 
-    const int ks = lane / LPK;                        // this lane's key slot
-    const int kc = (lane % LPK) * EK;                 // its first key column
-    const int uc = D >= 64 ? lane * EU : lane % D;    // its first write column
-    const bool u_owner = D >= 64 || lane < D;
+    const int ks = w * RW + lane / LPK;               // this lane's key slot
+    const int kj = lane % LPK;                        // its chunk phase
+    const int uc = w * DW + lane % DW;                // its write column
+    const int sg = lane / DW;                         // its slot group: slots [sg RS, (sg+1) RS)
 
     ST* Uh = (ST*)a.U + head * (R * D);
     ST* Kh = (ST*)a.K + head * (R * D);
     float* ch = a.c + head * R;
 
-    float Kr[EK];
-    load_run<ST, EK>(Kh + ks * D + kc, Kr);
-    float Ur[R][EU];
+    float Kr[NCH][CHE];
 #pragma unroll
-    for (int i = 0; i < R; ++i) load_run<ST, EU>(Uh + i * D + uc, Ur[i]);
-    float cw[R];
+    for (int m = 0; m < NCH; ++m)
+        load_run<ST, CHE, kLrStateNT>(Kh + ks * D + (m * LPK + kj) * CHE, Kr[m]);
+    float Ur[RS];
 #pragma unroll
-    for (int i = 0; i < R; ++i) cw[i] = uniform_f(ch[i]);
+    for (int i = 0; i < RS; ++i) {
+        float x[1];
+        load_run<ST, 1, kLrStateNT>(Uh + (sg * RS + i) * D + uc, x);
+        Ur[i] = x[0];
+    }
+    float cl[RS];   // weights of this lane's write slots
+#pragma unroll
+    for (int i = 0; i < RS; ++i) cl[i] = ch[sg * RS + i];
     const uint32_t p0 = (uint32_t)a.pos[head] & (uint32_t)(R - 1);
     uint32_t p = p0;
 
     for (int t = 0; t < a.T; ++t) {
         const int64_t g = (b * a.T + t) * a.H + h;     // (b, t, h)
-        const AT* kp = (const AT*)a.k + g * D + kc;
-        const AT* qp = (const AT*)a.q + g * D + kc;
-        float vt[EU];
-        load_run<AT, EU>((const AT*)a.v + g * D + uc, vt);
+        const AT* kp = (const AT*)a.k + g * D;
+        const AT* qp = (const AT*)a.q + g * D;
+        float vt[1];
+        load_run<AT, 1>((const AT*)a.v + g * D + uc, vt);
         const float al = a.alpha[g], be = a.beta[g];
 
-        // One pass over the window before this token: K_i . k, K_i . q and k . q (every key
-        // group holds the same columns of k and q, so its k . q total is the whole product).
+        // One pass over this wave's keys before the token: K_i . k, K_i . q and k . q (every
+        // slot's lanes cover all D columns of k and q, so a slot's k . q total is the whole
+        // product).
         float pa = 0.0f, pg = 0.0f, pkq = 0.0f;
 #pragma unroll
-        for (int c0 = 0; c0 < EK; c0 += KCH) {
-            float xk[KCH], xq[KCH];
-            load_run<AT, KCH>(kp + c0, xk);
-            load_run<AT, KCH>(qp + c0, xq);
+        for (int m = 0; m < NCH; ++m) {
+            float xk[CHE], xq[CHE];
+            load_run<AT, CHE>(kp + (m * LPK + kj) * CHE, xk);
+            load_run<AT, CHE>(qp + (m * LPK + kj) * CHE, xq);
 #pragma unroll
-            for (int e = 0; e < KCH; ++e) {
-                pa = fmaf(Kr[c0 + e], xk[e], pa);
-                pg = fmaf(Kr[c0 + e], xq[e], pg);
+            for (int e = 0; e < CHE; ++e) {
+                pa = fmaf(Kr[m][e], xk[e], pa);
+                pg = fmaf(Kr[m][e], xq[e], pg);
                 pkq = fmaf(xk[e], xq[e], pkq);
             }
         }
-        pa = group_sum<LPK>(pa);
-        pg = group_sum<LPK>(pg);
-        const float kq = lane_value(group_sum<LPK>(pkq), 0);
+        pa = slot_sum<LPK>(pa);
+        pg = slot_sum<LPK>(pg);
+        const float kq = lane_value(slot_sum<LPK>(pkq), 0);
+        // the lanes that hold a slot's writes need its totals: trade them through LDS (two
+        // buffers by token parity, so one barrier per token keeps every read before the
+        // buffer's next write)
+        if (kj == 0) {
+            xchg[t & 1][0][ks] = pa;
+            xchg[t & 1][1][ks] = pg;
+        }
+        __syncthreads();
 
-        // u = S k, and y = S q without the slot this token evicts; then
+        // u = S k, and y = S q without the slot this token evicts, over this lane's slots and
+        // then over the column's lanes; then
         //   delta = beta (v - alpha u),  o = scale (alpha y + (k . q) delta) = S_t (scale q).
-        float u[EU], y[EU];
+        float u = 0.0f, y = 0.0f;
 #pragma unroll
-        for (int e = 0; e < EU; ++e) u[e] = y[e] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const float wu = cw[i] * lane_value(pa, i * LPK);
-            const float wy = (uint32_t)i == p ? 0.0f : cw[i] * lane_value(pg, i * LPK);
-#pragma unroll
-            for (int e = 0; e < EU; ++e) {
-                u[e] = fmaf(wu, Ur[i][e], u[e]);
-                y[e] = fmaf(wy, Ur[i][e], y[e]);
-            }
+        for (int i = 0; i < RS; ++i) {
+            const int slot = sg * RS + i;
+            const float wu = cl[i] * xchg[t & 1][0][slot];
+            const float wy = (uint32_t)slot == p ? 0.0f : cl[i] * xchg[t & 1][1][slot];
+            u = fmaf(wu, Ur[i], u);
+            y = fmaf(wy, Ur[i], y);
         }
-        float o[EU];
-#pragma unroll
-        for (int e = 0; e < EU; ++e) {
-            const float d = be * fmaf(-al, u[e], vt[e]);
-            o[e] = a.scale * fmaf(al, y[e], kq * d);
-#pragma unroll
-            for (int i = 0; i < R; ++i) Ur[i][e] = (uint32_t)i == p ? d : Ur[i][e];
-        }
-        if (u_owner) store_run<AT, EU>((AT*)a.o + g * D + uc, o);
+        u = column_sum<SG, DW>(u);
+        y = column_sum<SG, DW>(y);
+        const float d = be * fmaf(-al, u, vt[0]);
+        float o[1] = {a.scale * fmaf(al, y, kq * d)};
+        if (sg == 0) store_run<AT, 1>((AT*)a.o + g * D + uc, o);
 
         // The decay of every stored write; the oldest slot takes (delta, k, 1).
 #pragma unroll
-        for (int i = 0; i < R; ++i) cw[i] = uniform_f((uint32_t)i == p ? 1.0f : cw[i] * al);
-        if ((uint32_t)ks == p) load_run<AT, EK>(kp, Kr);
+        for (int i = 0; i < RS; ++i) {
+            const bool mine = (uint32_t)(sg * RS + i) == p;
+            Ur[i] = mine ? d : Ur[i];
+            cl[i] = mine ? 1.0f : cl[i] * al;
+        }
+        if ((uint32_t)ks == p) {
+#pragma unroll
+            for (int m = 0; m < NCH; ++m) load_run<AT, CHE>(kp + (m * LPK + kj) * CHE, Kr[m]);
+        }
         p = (p + 1) & (uint32_t)(R - 1);
     }
 
     // Store the slots this call wrote, every weight, and the next slot.
     const uint32_t written = (uint32_t)(a.T < R ? a.T : R);
-    if (u_owner) {
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-            if ((((uint32_t)i - p0) & (uint32_t)(R - 1)) < written) store_run<ST, EU>(Uh + i * D + uc, Ur[i]);
+    for (int i = 0; i < RS; ++i)
+        if ((((uint32_t)(sg * RS + i) - p0) & (uint32_t)(R - 1)) < written) {
+            const float x[1] = {Ur[i]};
+            store_run<ST, 1>(Uh + (sg * RS + i) * D + uc, x);
+        }
+    if ((((uint32_t)ks - p0) & (uint32_t)(R - 1)) < written) {
+#pragma unroll
+        for (int m = 0; m < NCH; ++m) store_run<ST, CHE>(Kh + ks * D + (m * LPK + kj) * CHE, Kr[m]);
     }
-    if ((((uint32_t)ks - p0) & (uint32_t)(R - 1)) < written) store_run<ST, EK>(Kh + ks * D + kc, Kr);
-    float mine = 0.0f;
+    if (w == 0 && lane % DW == 0) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) mine = lane == i ? cw[i] : mine;
-    if (lane < R) ch[lane] = mine;
-    if (lane == 0) a.pos[head] = (int32_t)p;
+        for (int i = 0; i < RS; ++i) ch[sg * RS + i] = cl[i];
+        if (lane == 0) a.pos[head] = (int32_t)p;
+    }
 }
 
 template <int D, int R, typename AT, typename ST>
 hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
+    using G = LrGeo<D, R, AT, ST>;
     const int64_t heads = a.B * a.H;
-    const int64_t groups = (heads + kLowrankHeadsPerGroup - 1) / kLowrankHeadsPerGroup;
-    hipLaunchKernelGGL((gdn_lowrank_kernel<D, R, AT, ST>), dim3((uint32_t)groups),
-                       dim3(64 * kLowrankHeadsPerGroup), 0, stream, a);
+    hipLaunchKernelGGL((gdn_lowrank_kernel<D, R, AT, ST>), dim3((uint32_t)heads),
+                       dim3(64 * G::W), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -9,9 +9,9 @@
 
 namespace gdn {
 
-// One wave64 per (sequence, head), four heads per workgroup: B * H * 64 work-items per
-// launch, within the decode bound of 8 * D threads per head (D >= 16) that the caller checks.
-constexpr int kLowrankHeadsPerGroup = 4;
+// At most D / 32 wave64s per (sequence, head) (one below D = 64, at most four): at most 2 * D
+// work-items per head, within the decode bound of 8 * D threads per head that the caller
+// checks.
 
 struct LowrankArgs {
     int64_t B;
