@@ -171,3 +171,34 @@ def test_empty_calls_change_nothing():
     assert o.shape == (2, 0, 3, 64)
     for n in LOWRANK_STATE:
         assert torch.equal(g[n], before[n]), n
+
+
+def test_window_beyond_4_GiB_offsets():
+    # B=6144 x H=48 heads of a 32-slot fp32 window: U and K hold 4.8 GB each, so byte offsets
+    # pass 2^32. The window is drawn on the device from a seeded generator; sampled heads
+    # (including the last) are read back before the call and compared with the oracle.
+    _announce("lowrank B=6144 H=48 D=128 r=32 (2 x 4.8 GB window)")
+    B, H, D, r = 6144, 48, 128, 32
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    U = torch.randn(B, H, r, D, device="cuda", generator=gen).mul_(0.5)
+    K = torch.randn(B, H, r, D, device="cuda", generator=gen)
+    K /= K.norm(dim=-1, keepdim=True)
+    c = torch.rand(B, H, r, device="cuda", generator=gen)
+    pos = torch.randint(0, r, (B, H), device="cuda", generator=gen, dtype=torch.int32)
+    x = synth.lowrank_inputs(B, H, D, 1, r, act="bf16", window="empty", seed=13)
+    heads = sample_heads(B, H, 24, seed=13) + [(B - 1, 0), (B // 2, H - 1)]
+    bt, ht = (torch.as_tensor(a) for a in np.asarray(heads).T)
+    btd, htd = bt.cuda(), ht.cuda()
+    before = {n: t[btd, htd].cpu() for n, t in (("U", U), ("K", K), ("c", c), ("pos", pos))}
+    g = to_dev({n: x[n] for n in ("q", "k", "v", "alpha", "beta")})
+    o = gdn.lowrank_decode_step(g["q"], g["k"], g["v"], g["alpha"], g["beta"], U, K, c, pos)
+    torch.cuda.synchronize()
+    got = {n: t[btd, htd].cpu() for n, t in (("U", U), ("K", K), ("c", c), ("pos", pos))}
+    del U, K
+    sel = lambda t: f64(t[bt, :, ht])[:, :, None]
+    ref = oracle.gdn_lowrank_decode(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["alpha"]),
+                                    sel(x["beta"]), f64(before["U"])[:, None],
+                                    f64(before["K"])[:, None], f64(before["c"])[:, None],
+                                    before["pos"].numpy()[:, None])
+    ref = tuple(a[:, 0] for a in ref[:4]) + (ref[4][:, :, 0],)
+    check_lowrank(got, o.cpu()[bt, :, ht], ref, torch.bfloat16, torch.float32)
