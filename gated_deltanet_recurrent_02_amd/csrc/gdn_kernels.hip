@@ -968,11 +968,18 @@ hipError_t launch_fused_g(const FusedArgs& a, hipStream_t s) {
 
 constexpr int max_int(int a, int b) { return a > b ? a : b; }
 
+// Head count from which one-token fp32-state calls spread a head's tiles over the XCDs.
+constexpr int64_t kOneTokenSpreadHeads = 8192;
+
 // Launch geometry, chosen by sweeping variants on MI355X at B=256, H=48, D=128 (variants with
 // the same lanes per row reproduce each other bit for bit; only the schedule differs):
 //  * one token, fp32 state: one wave per workgroup, 8 rows (4 KiB) per wave, nontemporal
 //    state loads and stores -- 79% of HBM peak; larger workgroups synchronise their waves'
 //    load/store phases and lose 5-15%;
+//    Below 8192 heads the 16 tiles of a head stay on one XCD (its q, k and v are fetched into
+//    one L2): B = 8 .. 128 at H = 48 run 3-8% faster that way (B = 64: 70.4 -> 65.8 us),
+//    B = 160 and 192 tie, and B = 256 is 2% slower than with consecutive tiles on different
+//    XCDs, which it keeps;
 //  * one token, bf16 state: all rows of a head in one workgroup, 8 rows per wave, 8 lanes per
 //    row (two 16-byte loads per lane and row): 140 -> 130 us at B=256 H=48 D=128 against 16
 //    lanes per row (fp32 states show no difference);
@@ -991,6 +998,7 @@ template <int D, typename ST> struct DecodeOneToken {  // 2-byte states
 };
 template <int D> struct DecodeOneToken<D, float> {
     using G = Geo<D, float, 1, D / 8, 1, true, true>;
+    using G_small = Geo<D, float, 1, D / 8, 1, true, true, 2>;  // fewer than 8192 heads
 };
 
 template <int D, typename ST> struct DecodeTokens {  // 2-byte states
@@ -1016,6 +1024,10 @@ template <int D> struct FusedTokens<D, float> {
 
 template <int D, typename ST, typename AT>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+    if constexpr (sizeof(ST) == 4) {
+        if (a.T == 1 && a.B * a.H < kOneTokenSpreadHeads)
+            return launch_decode_g<typename DecodeOneToken<D, ST>::G_small, false, AT>(a, s);
+    }
     if (a.T == 1) return launch_decode_g<typename DecodeOneToken<D, ST>::G, false, AT>(a, s);
     return launch_decode_g<typename DecodeTokens<D, ST>::G, true, AT>(a, s);
 }
