@@ -150,9 +150,13 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x + lr_dpp<0x140>(x);                  // row_mirror: the other half of the row
 }
 
-// A value every lane holds identically, kept in a scalar register.
-__device__ __forceinline__ float uniform_f(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+// With U (true) a value every lane of the wave holds identically, kept in a scalar register.
+template <bool U>
+__device__ __forceinline__ float wave_uniform(float x) {
+    if constexpr (U)
+        return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+    else
+        return x;
 }
 
 __device__ __forceinline__ float lane_value(float x, int lane) {
@@ -221,7 +225,7 @@ template <int D, int R, typename AT, typename ST>
 __global__ __launch_bounds__((64 * LrGeo<D, R, AT, ST>::W))
 void gdn_lowrank_kernel(LowrankArgs a) {
     using G = LrGeo<D, R, AT, ST>;
-    constexpr int W = G::W, RW = G::RW, LPK = G::LPK, EK = G::EK, CHE = G::CHE, NCH = G::NCH;
+    constexpr int RW = G::RW, LPK = G::LPK, CHE = G::CHE, NCH = G::NCH;
     constexpr int DW = G::DW, SG = G::SG, RS = G::RS;
     __shared__ float xchg[2][2][R];   // [token parity][K.k, K.q][slot]
 
@@ -251,9 +255,9 @@ void gdn_lowrank_kernel(LowrankArgs a) {
         load_run<ST, 1, kLrStateNT>(Uh + (sg * RS + i) * D + uc, x);
         Ur[i] = x[0];
     }
-    float cl[RS];   // weights of this lane's write slots
+    float cl[RS];   // weights of this lane's write slots (scalar registers when SG == 1)
 #pragma unroll
-    for (int i = 0; i < RS; ++i) cl[i] = ch[sg * RS + i];
+    for (int i = 0; i < RS; ++i) cl[i] = wave_uniform<SG == 1>(ch[sg * RS + i]);
     const uint32_t p0 = (uint32_t)a.pos[head] & (uint32_t)(R - 1);
     uint32_t p = p0;
 
@@ -316,7 +320,7 @@ void gdn_lowrank_kernel(LowrankArgs a) {
         for (int i = 0; i < RS; ++i) {
             const bool mine = (uint32_t)(sg * RS + i) == p;
             Ur[i] = mine ? d : Ur[i];
-            cl[i] = mine ? 1.0f : cl[i] * al;
+            cl[i] = wave_uniform<SG == 1>(mine ? 1.0f : cl[i] * al);
         }
         if ((uint32_t)ks == p) {
 #pragma unroll
