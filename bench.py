@@ -18,6 +18,8 @@ is the measured HBM bytes per launch from a committed rocprofv3 counter summary,
 the kernel source changed since it was taken; `cpu_baseline` times the fp64 oracle on a
 bounded sample of the same workload on the host.
 
+The low-rank window workloads (`lowrank_*`) time gdn_lowrank_decode_step.
+
 `--workload copy_<MB>` instead times a plain device-to-device copy of that many MB (torch's
 copy kernel), the calibration used for the counter-based traffic and the practical
 read+write bandwidth ceiling.
