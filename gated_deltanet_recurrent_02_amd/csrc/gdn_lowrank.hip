@@ -221,7 +221,9 @@ __device__ __forceinline__ float column_sum(float x) {
 //     groups of a column;
 //   * pos is uniform across the workgroup; wave 0 stores the weights and pos.
 // One head per workgroup.
-template <int D, int R, typename AT, typename ST>
+// ONE: the call has one token (a separate instance: with the token count known, the keys are
+// dead after the key products and the other writes after the sums, which frees registers).
+template <int D, int R, typename AT, typename ST, bool ONE>
 __global__ __launch_bounds__((64 * LrGeo<D, R, AT, ST>::W))
 void gdn_lowrank_kernel(LowrankArgs a) {
     using G = LrGeo<D, R, AT, ST>;
@@ -261,7 +263,8 @@ void gdn_lowrank_kernel(LowrankArgs a) {
     const uint32_t p0 = (uint32_t)a.pos[head] & (uint32_t)(R - 1);
     uint32_t p = p0;
 
-    for (int t = 0; t < a.T; ++t) {
+    const int T = ONE ? 1 : a.T;
+    for (int t = 0; t < T; ++t) {
         const int64_t g = (b * a.T + t) * a.H + h;     // (b, t, h)
         const AT* kp = (const AT*)a.k + g * D;
         const AT* qp = (const AT*)a.q + g * D;
@@ -330,7 +333,7 @@ void gdn_lowrank_kernel(LowrankArgs a) {
     }
 
     // Store the slots this call wrote, every weight, and the next slot.
-    const uint32_t written = (uint32_t)(a.T < R ? a.T : R);
+    const uint32_t written = (uint32_t)(T < R ? T : R);
 #pragma unroll
     for (int i = 0; i < RS; ++i)
         if ((((uint32_t)(sg * RS + i) - p0) & (uint32_t)(R - 1)) < written) {
@@ -352,8 +355,12 @@ template <int D, int R, typename AT, typename ST>
 hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
     using G = LrGeo<D, R, AT, ST>;
     const int64_t heads = a.B * a.H;
-    hipLaunchKernelGGL((gdn_lowrank_kernel<D, R, AT, ST>), dim3((uint32_t)heads),
-                       dim3(64 * G::W), 0, stream, a);
+    if (a.T == 1)
+        hipLaunchKernelGGL((gdn_lowrank_kernel<D, R, AT, ST, true>), dim3((uint32_t)heads),
+                           dim3(64 * G::W), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gdn_lowrank_kernel<D, R, AT, ST, false>), dim3((uint32_t)heads),
+                           dim3(64 * G::W), 0, stream, a);
     return hipGetLastError();
 }
 
