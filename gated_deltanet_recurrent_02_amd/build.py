@@ -33,9 +33,24 @@ HIPFLAGS = [
 
 
 def build(output: str = LIBRARY, extra_flags: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile the kernels and the C ABI into one shared library; returns its path."""
+    """Compile the kernels and the C ABI into one shared library; returns its path. Each source
+    compiles to an object of its own, all at once, and one hipcc call links them."""
+    objdir = os.path.join(os.path.dirname(os.path.abspath(output)), "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cflags = [f for f in HIPFLAGS if f != "-shared"]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *cflags, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}", "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append((cmd, subprocess.Popen(cmd)))
+    failed = [cmd for cmd, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = output + ".tmp"
-    cmd = [HIPCC, *HIPFLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp, *SOURCES]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
