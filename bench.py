@@ -269,6 +269,9 @@ def time_gpu(args, spec, workload):
             per.append(e0.elapsed_time(e1) / args.graph_replays)
         per.sort()
         extra["graph_median_us"] = per[len(per) // 2] * 1e3
+        # spread over the groups: nearest-rank 10th and 90th percentiles of the group means
+        extra["graph_p10_us"] = per[max(0, math.ceil(0.1 * len(per)) - 1)] * 1e3
+        extra["graph_p90_us"] = per[max(0, math.ceil(0.9 * len(per)) - 1)] * 1e3
         extra["graph_protocol"] = f"median of {args.graph_groups} graph replays x {args.graph_replays} launches"
         del g
     # Plain device copy of the same number of state bytes: the read+write ceiling of this machine.
