@@ -202,3 +202,45 @@ def test_window_beyond_4_GiB_offsets():
                                     before["pos"].numpy()[:, None])
     ref = tuple(a[:, 0] for a in ref[:4]) + (ref[4][:, :, 0],)
     check_lowrank(got, o.cpu()[bt, :, ht], ref, torch.bfloat16, torch.float32)
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_identity_gate_replaces_only_the_oldest_slot(sdt):
+    # alpha = 1, beta = 0: the write is exactly zero and no weight changes, so the call only
+    # moves the oldest slot to (0, k, 1); every other slot, weight and key is untouched, bit
+    # for bit.
+    _announce(f"lowrank identity gate state={sdt}")
+    x = synth.lowrank_inputs(3, 5, 128, 1, 16, act="bf16", state_dtype=sdt, seed=14)
+    x["alpha"][:] = 1.0
+    x["beta"][:] = 0.0
+    g, o = gpu_lowrank(x)
+    p = (x["pos"].long() & 15)
+    B, H = p.shape
+    for b in range(B):
+        for h in range(H):
+            pi = int(p[b, h])
+            keep = [i for i in range(16) if i != pi]
+            assert torch.equal(g["U"][b, h, keep].cpu(), x["U"][b, h, keep]), (b, h)
+            assert torch.equal(g["K"][b, h, keep].cpu(), x["K"][b, h, keep]), (b, h)
+            assert torch.equal(g["c"][b, h, keep].cpu(), x["c"][b, h, keep]), (b, h)
+            assert bool((g["U"][b, h, pi] == 0).all()) and float(g["c"][b, h, pi]) == 1.0
+            assert torch.equal(g["K"][b, h, pi].cpu(), x["k"][b, 0, h].to(DT[sdt]))
+    assert torch.equal(g["pos"].cpu(), ((p + 1) % 16).int())
+    check_lowrank(g, o, oracle_lowrank(x), torch.bfloat16, DT[sdt])
+
+
+def test_zero_decay_keeps_only_the_new_write():
+    # alpha = 0: every earlier write's weight becomes exactly 0, the new slot's 1, and the
+    # write is beta v (S k is multiplied by 0), so o = scale beta (k . q) v.
+    _announce("lowrank zero decay")
+    x = synth.lowrank_inputs(2, 4, 64, 1, 8, act="f32", seed=15)
+    x["alpha"][:] = 0.0
+    g, o = gpu_lowrank(x, scale=0.5)
+    p = (x["pos"].long() & 7)
+    for b in range(2):
+        for h in range(4):
+            c = g["c"][b, h].cpu()
+            expect = torch.zeros(8)
+            expect[int(p[b, h])] = 1.0
+            assert torch.equal(c, expect), (b, h)
+    check_lowrank(g, o, oracle_lowrank(x, scale=0.5), torch.float32, torch.float32)
