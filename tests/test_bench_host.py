@@ -38,3 +38,20 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_algorithmic_bytes_of_the_low_rank_workloads():
+    # r = 16 slots, fp32 window, bf16 q/k/v/o, one token: per head the window is read once
+    # (U and K: 2 * 16 * 128 * 4 B, weights 16 * 4 B, pos 4 B); the token's slot (U and K rows,
+    # 2 * 128 * 4 B), every weight and pos are written; q, k, v, alpha, beta read, o written.
+    read = 2 * 16 * 128 * 4 + 16 * 4 + 4
+    write = 2 * 128 * 4 + 16 * 4 + 4
+    token = 3 * 128 * 2 + 8 + 128 * 2
+    assert read + write + token == 18576
+    spec = synth.WORKLOADS["lowrank_b256_h48_d128_r16_t1"]
+    assert bench.algorithmic_bytes(spec, "f32") == 256 * 48 * 18576 == 228261888
+    # four tokens write four slots; a bf16 window halves the U and K bytes
+    spec4 = synth.WORKLOADS["lowrank_b256_h48_d128_r16_t4"]
+    read16 = 2 * 16 * 128 * 2 + 16 * 4 + 4
+    write16 = 4 * 2 * 128 * 2 + 16 * 4 + 4
+    assert bench.algorithmic_bytes(spec4, "bf16") == 256 * 48 * (read16 + write16 + 4 * token)
