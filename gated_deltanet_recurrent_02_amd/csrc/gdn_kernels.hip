@@ -975,7 +975,8 @@ constexpr int64_t kOneTokenSpreadHeads = 8192;
 // the same lanes per row reproduce each other bit for bit; only the schedule differs):
 //  * one token, fp32 state: one wave per workgroup, 8 rows (4 KiB) per wave, nontemporal
 //    state loads and stores -- 79% of HBM peak; larger workgroups synchronise their waves'
-//    load/store phases and lose 5-15%;
+//    load/store phases and lose 5-15%; 16 rows per wave (256 -> 278 us at B = 256) and 4 rows
+//    per wave (-> 294 us) lose too;
 //    Below 8192 heads the 16 tiles of a head stay on one XCD (its q, k and v are fetched into
 //    one L2): B = 8 .. 128 at H = 48 run 3-8% faster that way (B = 64: 70.4 -> 65.8 us),
 //    B = 160 and 192 tie, and B = 256 is 2% slower than with consecutive tiles on different
