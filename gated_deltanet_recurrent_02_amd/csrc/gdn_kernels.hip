@@ -989,7 +989,8 @@ constexpr int64_t kOneTokenSpreadHeads = 8192;
 //    8 lanes per row where it saves reduction steps (bf16 state, fused prologue);
 //  * several tokens, fp32 state, decode: one wave per workgroup again (16 rows, the 8 tiles
 //    of a head kept on one XCD so its q and k come from one L2): 2% faster than a workgroup
-//    per head at B=256 H=48 D=128 T=4, where the verify kernel is 3% slower with it;
+//    per head at B=256 H=48 D=128 T=4, where the verify kernel is 3% slower with it; 8 rows
+//    per wave (16 tiles per head) is slower (277 -> 302 us);
 //  * fused path, fp32 state: 4 waves of 32 rows per head (190 VGPRs, two workgroups per CU):
 //    2.5% faster than 8 waves of 16 rows at B=256 H=48 D=128 T=4; 16-bit states lose 9% with
 //    it. The fused kernel needs the whole head in one workgroup (the conv state of the q and
