@@ -172,6 +172,8 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
 template <int R, typename ST>
 constexpr int lr_max_waves() { return sizeof(ST) == 4 && R >= 32 ? 4 : 2; }
 constexpr bool kLrStateNT = true;
+// Tokens per staged round of a multi-token call.
+constexpr int kLrRound = 8;
 
 // Geometry of one instance: head dim D, window R, storage types AT (activations), ST (state).
 template <int D, int R, typename AT, typename ST>
@@ -230,6 +232,10 @@ void gdn_lowrank_kernel(LowrankArgs a) {
     constexpr int RW = G::RW, LPK = G::LPK, CHE = G::CHE, NCH = G::NCH;
     constexpr int DW = G::DW, SG = G::SG, RS = G::RS;
     __shared__ float xchg[2][2][R];   // [token parity][K.k, K.q][slot]
+    // multi-token calls: the tokens of a round of up to kLrRound, staged once per round
+    constexpr int TS = ONE ? 1 : kLrRound;
+    __shared__ alignas(16) float tok[ONE ? 1 : 3][TS][ONE ? 4 : D];   // [k, q, v][token][column]
+    __shared__ float tok_ab[ONE ? 1 : 2][TS];                           // [alpha, beta][token]
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave within the head
@@ -268,9 +274,42 @@ void gdn_lowrank_kernel(LowrankArgs a) {
         const int64_t g = (b * a.T + t) * a.H + h;     // (b, t, h)
         const AT* kp = (const AT*)a.k + g * D;
         const AT* qp = (const AT*)a.q + g * D;
+        const int tt = ONE ? 0 : t % kLrRound;        // the token's place in its round
+        if constexpr (!ONE) {
+            if (tt == 0) {
+                // stage the round's k, q and v rows (16-byte chunks over the workgroup) and
+                // gates; the barrier also ends the previous round's reads of the buffer
+                constexpr int CK = 16 / (int)sizeof(AT), NCR = D / CK;
+                const int nt = min(kLrRound, T - t);
+                __syncthreads();
+                for (int c = threadIdx.x; c < nt * 3 * NCR; c += 64 * G::W) {
+                    const int j = c / NCR, col = (c - j * NCR) * CK, which = j / nt, u = j - which * nt;
+                    const AT* src = which == 0 ? (const AT*)a.k : which == 1 ? (const AT*)a.q
+                                                                            : (const AT*)a.v;
+                    float x[CK];
+                    load_run<AT, CK>(src + ((b * a.T + t + u) * a.H + h) * D + col, x);
+#pragma unroll
+                    for (int e = 0; e < CK; ++e) tok[which][u][col + e] = x[e];
+                }
+                if ((int)threadIdx.x < nt) {
+                    const int64_t gu = (b * a.T + t + threadIdx.x) * a.H + h;
+                    tok_ab[0][threadIdx.x] = a.alpha[gu];
+                    tok_ab[1][threadIdx.x] = a.beta[gu];
+                }
+                __syncthreads();
+            }
+        }
         float vt[1];
-        load_run<AT, 1>((const AT*)a.v + g * D + uc, vt);
-        const float al = a.alpha[g], be = a.beta[g];
+        float al, be;
+        if constexpr (ONE) {
+            load_run<AT, 1>((const AT*)a.v + g * D + uc, vt);
+            al = a.alpha[g];
+            be = a.beta[g];
+        } else {
+            vt[0] = tok[2][tt][uc];
+            al = wave_uniform<true>(tok_ab[0][tt]);
+            be = wave_uniform<true>(tok_ab[1][tt]);
+        }
 
         // One pass over this wave's keys before the token: K_i . k, K_i . q and k . q (every
         // slot's lanes cover all D columns of k and q, so a slot's k . q total is the whole
@@ -279,8 +318,16 @@ void gdn_lowrank_kernel(LowrankArgs a) {
 #pragma unroll
         for (int m = 0; m < NCH; ++m) {
             float xk[CHE], xq[CHE];
-            load_run<AT, CHE>(kp + (m * LPK + kj) * CHE, xk);
-            load_run<AT, CHE>(qp + (m * LPK + kj) * CHE, xq);
+            if constexpr (ONE) {
+                load_run<AT, CHE>(kp + (m * LPK + kj) * CHE, xk);
+                load_run<AT, CHE>(qp + (m * LPK + kj) * CHE, xq);
+            } else {
+#pragma unroll
+                for (int e = 0; e < CHE; ++e) {
+                    xk[e] = tok[0][tt][(m * LPK + kj) * CHE + e];
+                    xq[e] = tok[1][tt][(m * LPK + kj) * CHE + e];
+                }
+            }
 #pragma unroll
             for (int e = 0; e < CHE; ++e) {
                 pa = fmaf(Kr[m][e], xk[e], pa);
@@ -327,7 +374,14 @@ void gdn_lowrank_kernel(LowrankArgs a) {
         }
         if ((uint32_t)ks == p) {
 #pragma unroll
-            for (int m = 0; m < NCH; ++m) load_run<AT, CHE>(kp + (m * LPK + kj) * CHE, Kr[m]);
+            for (int m = 0; m < NCH; ++m) {
+                if constexpr (ONE) {
+                    load_run<AT, CHE>(kp + (m * LPK + kj) * CHE, Kr[m]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < CHE; ++e) Kr[m][e] = tok[0][tt][(m * LPK + kj) * CHE + e];
+                }
+            }
         }
         p = (p + 1) & (uint32_t)(R - 1);
     }
