@@ -67,8 +67,8 @@ def test_verify_rounds_commit_the_accepted_prefix(D, sdt):
     S2c = _oracle_prefix(S1c, x2, n2.tolist())
     check_o(f64(o1), o1_ref, torch.bfloat16)
     check_o(f64(o2), o2_ref, torch.bfloat16)
-    check_state(f64(S_after2), S1c, DT[sdt], what="committed state after round 1")
-    check_state(f64(state), S2c, DT[sdt], what="committed state after round 2")
+    check_state(f64(S_after2), S1c, DT[sdt], what="committed state after the first verify call")
+    check_state(f64(state), S2c, DT[sdt], what="committed state after the second verify call")
 
 
 def test_verify_write_coefficients():
