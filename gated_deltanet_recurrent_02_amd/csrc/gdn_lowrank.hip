@@ -189,10 +189,13 @@ struct LrGeo {
     static constexpr int CHE = (16 / (int)sizeof(ST)) < EK ? (16 / (int)sizeof(ST)) : EK;
     static constexpr int NCH = EK / CHE;                  // key chunks per lane
     static constexpr int DW = D / W;                      // write columns per wave
-    static constexpr int SG = 64 / DW;                    // lanes per write column
+    // write columns per lane: two for 16-bit windows (4-byte loads), else one
+    static constexpr int EU = sizeof(ST) == 2 && DW >= 64 ? 2 : 1;
+    static constexpr int CL = DW / EU;                    // lanes that cover the wave's columns
+    static constexpr int SG = 64 / CL;                    // lanes per write column
     static constexpr int RS = R / SG;                     // write slots per lane
     static_assert(LPK >= 2 && LPK <= 16 && EK * LPK == D && NCH * CHE == EK, "key layout");
-    static_assert(DW <= 64 && SG * DW == 64 && (SG == 1 || SG == 2 || SG == 4) && RS >= 1,
+    static_assert(CL <= 64 && SG * CL == 64 && (SG == 1 || SG == 2 || SG == 4) && RS >= 1,
                   "write layout");
 };
 
@@ -217,10 +220,11 @@ __device__ __forceinline__ float column_sum(float x) {
 //     LPK * 16 contiguous bytes of each of RW rows). K_i . k and K_i . q reduce across the
 //     slot's lanes with DPP, and the slot totals go through LDS (one barrier per token) to
 //     the lanes that hold that slot's writes;
-//   * writes: the wave owns columns [w DW, (w+1) DW) of every slot's U; lane l holds column
-//     w DW + l mod DW of the RS slots of its slot group l / DW, with those slots' weights, so
-//     u, y, delta and o are lane-local sums over slots plus one cross-lane sum over the SG
-//     groups of a column;
+//   * writes: the wave owns columns [w DW, (w+1) DW) of every slot's U; lane l holds the EU
+//     adjacent columns starting at w DW + (l mod CL) EU (EU = 2 for 16-bit windows, so each
+//     load is 4 bytes; else 1) of the RS slots of its slot group l / CL, with those slots'
+//     weights, so u, y, delta and o are lane-local sums over slots plus one cross-lane sum
+//     over the SG groups of a column;
 //   * pos is uniform across the workgroup; wave 0 stores the weights and pos.
 // One head per workgroup.
 // ONE: the call has one token (a separate instance: with the token count known, the keys are
@@ -230,7 +234,7 @@ __global__ __launch_bounds__((64 * LrGeo<D, R, AT, ST>::W))
 void gdn_lowrank_kernel(LowrankArgs a) {
     using G = LrGeo<D, R, AT, ST>;
     constexpr int RW = G::RW, LPK = G::LPK, CHE = G::CHE, NCH = G::NCH;
-    constexpr int DW = G::DW, SG = G::SG, RS = G::RS;
+    constexpr int DW = G::DW, SG = G::SG, RS = G::RS, EU = G::EU, CL = G::CL;
     __shared__ float xchg[2][2][R];   // [token parity][K.k, K.q][slot]
     // multi-token calls: the tokens of a round of up to kLrRound, staged once per round
     constexpr int TS = ONE ? 1 : kLrRound;
@@ -245,8 +249,8 @@ void gdn_lowrank_kernel(LowrankArgs a) {
 
     const int ks = w * RW + lane / LPK;               // this lane's key slot
     const int kj = lane % LPK;                        // its chunk phase
-    const int uc = w * DW + lane % DW;                // its write column
-    const int sg = lane / DW;                         // its slot group: slots [sg RS, (sg+1) RS)
+    const int uc = w * DW + (lane % CL) * EU;         // its first write column
+    const int sg = lane / CL;                         // its slot group: slots [sg RS, (sg+1) RS)
 
     ST* Uh = (ST*)a.U + head * (R * D);
     ST* Kh = (ST*)a.K + head * (R * D);
@@ -256,13 +260,9 @@ void gdn_lowrank_kernel(LowrankArgs a) {
 #pragma unroll
     for (int m = 0; m < NCH; ++m)
         load_run<ST, CHE, kLrStateNT>(Kh + ks * D + (m * LPK + kj) * CHE, Kr[m]);
-    float Ur[RS];
+    float Ur[RS][EU];
 #pragma unroll
-    for (int i = 0; i < RS; ++i) {
-        float x[1];
-        load_run<ST, 1, kLrStateNT>(Uh + (sg * RS + i) * D + uc, x);
-        Ur[i] = x[0];
-    }
+    for (int i = 0; i < RS; ++i) load_run<ST, EU, kLrStateNT>(Uh + (sg * RS + i) * D + uc, Ur[i]);
     float cl[RS];   // weights of this lane's write slots (scalar registers when SG == 1)
 #pragma unroll
     for (int i = 0; i < RS; ++i) cl[i] = wave_uniform<SG == 1>(ch[sg * RS + i]);
@@ -299,14 +299,15 @@ void gdn_lowrank_kernel(LowrankArgs a) {
                 __syncthreads();
             }
         }
-        float vt[1];
+        float vt[EU];
         float al, be;
         if constexpr (ONE) {
-            load_run<AT, 1>((const AT*)a.v + g * D + uc, vt);
+            load_run<AT, EU>((const AT*)a.v + g * D + uc, vt);
             al = a.alpha[g];
             be = a.beta[g];
         } else {
-            vt[0] = tok[2][tt][uc];
+#pragma unroll
+            for (int e = 0; e < EU; ++e) vt[e] = tok[2][tt][uc + e];
             al = wave_uniform<true>(tok_ab[0][tt]);
             be = wave_uniform<true>(tok_ab[1][tt]);
         }
@@ -350,26 +351,36 @@ void gdn_lowrank_kernel(LowrankArgs a) {
         // u = S k, and y = S q without the slot this token evicts, over this lane's slots and
         // then over the column's lanes; then
         //   delta = beta (v - alpha u),  o = scale (alpha y + (k . q) delta) = S_t (scale q).
-        float u = 0.0f, y = 0.0f;
+        float u[EU], y[EU];
+#pragma unroll
+        for (int e = 0; e < EU; ++e) u[e] = y[e] = 0.0f;
 #pragma unroll
         for (int i = 0; i < RS; ++i) {
             const int slot = sg * RS + i;
             const float wu = cl[i] * xchg[t & 1][0][slot];
             const float wy = (uint32_t)slot == p ? 0.0f : cl[i] * xchg[t & 1][1][slot];
-            u = fmaf(wu, Ur[i], u);
-            y = fmaf(wy, Ur[i], y);
+#pragma unroll
+            for (int e = 0; e < EU; ++e) {
+                u[e] = fmaf(wu, Ur[i][e], u[e]);
+                y[e] = fmaf(wy, Ur[i][e], y[e]);
+            }
         }
-        u = column_sum<SG, DW>(u);
-        y = column_sum<SG, DW>(y);
-        const float d = be * fmaf(-al, u, vt[0]);
-        float o[1] = {a.scale * fmaf(al, y, kq * d)};
-        if (sg == 0) store_run<AT, 1>((AT*)a.o + g * D + uc, o);
+        float d[EU], o[EU];
+#pragma unroll
+        for (int e = 0; e < EU; ++e) {
+            u[e] = column_sum<SG, CL>(u[e]);
+            y[e] = column_sum<SG, CL>(y[e]);
+            d[e] = be * fmaf(-al, u[e], vt[e]);
+            o[e] = a.scale * fmaf(al, y[e], kq * d[e]);
+        }
+        if (sg == 0) store_run<AT, EU>((AT*)a.o + g * D + uc, o);
 
         // The decay of every stored write; the oldest slot takes (delta, k, 1).
 #pragma unroll
         for (int i = 0; i < RS; ++i) {
             const bool mine = (uint32_t)(sg * RS + i) == p;
-            Ur[i] = mine ? d : Ur[i];
+#pragma unroll
+            for (int e = 0; e < EU; ++e) Ur[i][e] = mine ? d[e] : Ur[i][e];
             cl[i] = wave_uniform<SG == 1>(mine ? 1.0f : cl[i] * al);
         }
         if ((uint32_t)ks == p) {
@@ -390,15 +401,13 @@ void gdn_lowrank_kernel(LowrankArgs a) {
     const uint32_t written = (uint32_t)(T < R ? T : R);
 #pragma unroll
     for (int i = 0; i < RS; ++i)
-        if ((((uint32_t)(sg * RS + i) - p0) & (uint32_t)(R - 1)) < written) {
-            const float x[1] = {Ur[i]};
-            store_run<ST, 1>(Uh + (sg * RS + i) * D + uc, x);
-        }
+        if ((((uint32_t)(sg * RS + i) - p0) & (uint32_t)(R - 1)) < written)
+            store_run<ST, EU>(Uh + (sg * RS + i) * D + uc, Ur[i]);
     if ((((uint32_t)ks - p0) & (uint32_t)(R - 1)) < written) {
 #pragma unroll
         for (int m = 0; m < NCH; ++m) store_run<ST, CHE>(Kh + ks * D + (m * LPK + kj) * CHE, Kr[m]);
     }
-    if (w == 0 && lane % DW == 0) {
+    if (w == 0 && lane % CL == 0) {
 #pragma unroll
         for (int i = 0; i < RS; ++i) ch[sg * RS + i] = cl[i];
         if (lane == 0) a.pos[head] = (int32_t)p;
