@@ -357,8 +357,11 @@ void gdn_lowrank_kernel(LowrankArgs a) {
 #pragma unroll
         for (int i = 0; i < RS; ++i) {
             const int slot = sg * RS + i;
+            // both products unconditionally, then a select: a conditional product would be
+            // compiled as a branch around its LDS read, one wait per slot
             const float wu = cl[i] * xchg[t & 1][0][slot];
-            const float wy = (uint32_t)slot == p ? 0.0f : cl[i] * xchg[t & 1][1][slot];
+            const float wg = cl[i] * xchg[t & 1][1][slot];
+            const float wy = (uint32_t)slot == p ? 0.0f : wg;
 #pragma unroll
             for (int e = 0; e < EU; ++e) {
                 u[e] = fmaf(wu, Ur[i][e], u[e]);
