@@ -508,7 +508,32 @@ def pin_lowrank_calls_resume(lib, seed=25):
     assert np.array_equal(whole[4], np.concatenate(outs, axis=1))
 
 
-LOWRANK_PINS = [pin_lowrank_long_window_is_full_rank, pin_lowrank_orthogonal_keys,
+def pin_lowrank_golden_worked(lib):
+    """Hand-worked dyadic examples of the window (golden/gdn_lowrank_worked.json) reproduce
+    exactly, token by token and in one call."""
+    with open(os.path.join(GOLDEN, "gdn_lowrank_worked.json")) as f:
+        doc = json.load(f)
+    for case in doc["cases"]:
+        toks = case["tokens"]
+        T = len(toks)
+        q = np.array([[t["q"] for t in toks]], dtype=float)[:, :, None, :]
+        k = np.array([[t["k"] for t in toks]], dtype=float)[:, :, None, :]
+        v = np.array([[t["v"] for t in toks]], dtype=float)[:, :, None, :]
+        al = np.array([[t["alpha"] for t in toks]], dtype=float)[:, :, None]
+        be = np.array([[t["beta"] for t in toks]], dtype=float)[:, :, None]
+        U0 = np.array(case["U0"], dtype=float)[None, None]
+        K0 = np.array(case["K0"], dtype=float)[None, None]
+        c0 = np.array(case["c0"], dtype=float)[None, None]
+        pos0 = np.array([[case["pos0"]]], dtype=np.int32)
+        U, K, c, pos, o = oracle.gdn_lowrank_decode(q, k, v, al, be, U0, K0, c0, pos0, lib=lib)
+        assert np.array_equal(o[0, :, 0, :], np.array([t["o"] for t in toks], dtype=float)), case["name"]
+        assert np.array_equal(U[0, 0], np.array(case["U"], dtype=float)), case["name"]
+        assert np.array_equal(K[0, 0], np.array(case["K"], dtype=float)), case["name"]
+        assert np.array_equal(c[0, 0], np.array(case["c"], dtype=float)), case["name"]
+        assert int(pos[0, 0]) == case["pos"] and o.shape == (1, T, 1, 2), case["name"]
+
+
+LOWRANK_PINS = [pin_lowrank_golden_worked, pin_lowrank_long_window_is_full_rank, pin_lowrank_orthogonal_keys,
                 pin_lowrank_single_slot, pin_lowrank_rank_bound, pin_lowrank_bruteforce,
                 pin_lowrank_calls_resume]
 
