@@ -107,6 +107,32 @@ def oracle_decode_all(x: dict, scale: float = 1.0, workers: int = 0):
             o.reshape(B, H, T, dv).transpose(0, 2, 1, 3))
 
 
+def per_sequence(fn, B: int, workers: int = 0) -> list:
+    """fn(b) for every sequence b on a thread pool (the C oracle runs outside the GIL);
+    results in sequence order."""
+    workers = workers or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(min(workers, B)) as ex:
+        return list(ex.map(fn, range(B)))
+
+
+def oracle_prefix_all(x: dict, n, state: np.ndarray | None = None, workers: int = 0):
+    """Per sequence b, the oracle's state after the first n[b] tokens of x (clamped to
+    [0, T]), starting from `state` (fp64 [B,H,dv,dk]; x's state if None). Returns the fp64
+    state [B,H,dv,dk]; sequences with an empty prefix keep their start state."""
+    S0 = f64(x["state"]) if state is None else state
+    T = x["T"]
+    n = [min(max(int(v), 0), T) for v in n]
+
+    def one(b):
+        if n[b] == 0:
+            return S0[b:b + 1]
+        sl = slice(0, n[b])
+        toks = [f64(x[m][b:b + 1, sl]) for m in ("q", "k", "v", "alpha", "beta")]
+        return oracle.gdn_decode(*toks, S0[b:b + 1])[0]
+
+    return np.concatenate(per_sequence(one, x["B"], workers))
+
+
 def sample_heads(B: int, H: int, n: int, seed: int = 0):
     """The first and last head plus n random (b, h) pairs."""
     rng = np.random.default_rng(seed)
@@ -152,8 +178,9 @@ def oracle_lowrank(x: dict, scale: float = 1.0, heads=None):
 
 
 def effective_state(U: np.ndarray, K: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """sum_i c_i U_i K_i^T over the slot axis (third from last of U)."""
-    return np.einsum("...s,...si,...sj->...ij", c, U, K)
+    """sum_i c_i U_i K_i^T over the slot axis (third from last of U), as one batched
+    product (c-weighted U)^T K."""
+    return np.matmul(np.swapaxes(U * c[..., None], -1, -2), K)
 
 
 def check_lowrank(got: dict, o, ref, act: torch.dtype, sdt: torch.dtype):
