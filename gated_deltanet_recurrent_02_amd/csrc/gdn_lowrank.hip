@@ -421,13 +421,13 @@ template <int D, int R, typename AT, typename ST>
 hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
     using G = LrGeo<D, R, AT, ST>;
     const int64_t heads = a.B * a.H;
-    if (a.T == 1)
-        hipLaunchKernelGGL((gdn_lowrank_kernel<D, R, AT, ST, true>), dim3((uint32_t)heads),
-                           dim3(64 * G::W), 0, stream, a);
-    else
-        hipLaunchKernelGGL((gdn_lowrank_kernel<D, R, AT, ST, false>), dim3((uint32_t)heads),
-                           dim3(64 * G::W), 0, stream, a);
-    return hipGetLastError();
+    // The launch's own status (not hipGetLastError, which would also report, and clear, an
+    // error left on this thread by an earlier, unrelated HIP call).
+    LowrankArgs args = a;
+    void* argv[] = {&args};
+    const void* fn = a.T == 1 ? (const void*)gdn_lowrank_kernel<D, R, AT, ST, true>
+                              : (const void*)gdn_lowrank_kernel<D, R, AT, ST, false>;
+    return hipLaunchKernel(fn, dim3((uint32_t)heads), dim3(64 * G::W), argv, 0, stream);
 }
 
 template <int D, typename AT, typename ST>
