@@ -55,3 +55,96 @@ def test_algorithmic_bytes_of_the_low_rank_workloads():
     read16 = 2 * 16 * 128 * 2 + 16 * 4 + 4
     write16 = 4 * 2 * 128 * 2 + 16 * 4 + 4
     assert bench.algorithmic_bytes(spec4, "bf16") == 256 * 48 * (read16 + write16 + 4 * token)
+
+
+def test_prefill_matrix_flops_of_the_prompt_workload():
+    # Per head and chunk of 16 tokens, D = 128: K S'^T and Q S'^T on three bf16 parts
+    # (3 x 2 x 16 x 128 x 128 x 2), the update on three parts (3 x 128 x 16 x 128 x 2), K Q^T and
+    # the prep's K K^T (2 x 16 x 16 x 128 x 2) in bf16; T Z and P Delta (2 x 16 x 16 x 128 x 2)
+    # in fp32. 4 x 48 heads x 256 chunks.
+    spec = synth.WORKLOADS["prefill_b4_h48_d128_t4096"]
+    f = bench.prefill_matrix_flops(spec)
+    per_chunk_bf16 = 3 * 2 * 16 * 128 * 128 * 2 + 3 * 128 * 16 * 128 * 2 + 2 * 16 * 16 * 128 * 2
+    assert f["bf16"] == 4 * 48 * 256 * per_chunk_bf16
+    assert f["f32"] == 4 * 48 * 256 * 2 * 16 * 16 * 128 * 2
+    # the method's own arithmetic: 6 D^2 + 6 D per token and head
+    assert bench.flops(spec) == 4 * 48 * 4096 * (6 * 128 * 128 + 6 * 128)
+
+
+def test_profile_commands_run_committed_files_only():
+    cmds = dict(bench.profile_commands("decode_b256_h48_d128_t4", "bf16", "gpurun_out"))
+    assert set(cmds) == {"bench", "trace", "fetch", "write", "req", "wreq", "sq", "vb"}
+    for name, c in cmds.items():
+        assert "_work" not in c and "python bench.py --workload decode_b256_h48_d128_t4" in c
+        if name not in ("bench", "trace"):
+            assert c.startswith("rocprofv3 --pmc ") and "--sys-trace" not in c
+    # at most 8 SQ, 4 TCC and 2 GRBM counters per pass
+    sq = cmds["sq"].split("--pmc ")[1].split(" -d ")[0].split()
+    assert sum(c.startswith("SQ_") for c in sq) <= 8 and sum(c.startswith("GRBM_") for c in sq) <= 2
+    req = cmds["req"].split("--pmc ")[1].split(" -d ")[0].split()
+    assert len(req) <= 4 and all(c.startswith("TCC_") for c in req)
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_summarize_reads_rocprof_csvs(tmp_path):
+    # Synthetic rocprofv3 outputs for the headline workload: the summary must add up the
+    # counters exactly as documented (copy calibration, request sizes, per-wave counts).
+    root = str(tmp_path / "prof")
+    tag = "decode_b256_h48_d128_t1_f32"
+    kname = "void gdn::gdn_decode_kernel<Geo>(int)"
+    _write_csv(f"{root}/prof_trace_{tag}/k_kernel_stats.csv",
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+               [[kname, 10, 2_600_000, 260_000.0, 99.0, 250_000, 270_000, 100.0],
+                ["__amd_rocclr_copyBuffer", 2, 600_000, 300_000.0, 1.0, 290_000, 310_000, 5.0]])
+    hdr = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+           "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+           "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+           "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+    def rows(values, name=kname):
+        out = []
+        for d in (1, 2):
+            for c, v in values.items():
+                out.append([d, d, "Agent 1", 1, 1, 1, 196608, 4, name, 64, 2560, 0, 40, 0, 24, c, v, 0, 1])
+        return out
+
+    _write_csv(f"{root}/prof_fetch_{tag}/k_counter_collection.csv", hdr, rows({"FETCH_SIZE": 400_000.0}))
+    _write_csv(f"{root}/prof_write_{tag}/k_counter_collection.csv", hdr, rows({"WRITE_SIZE": 800_000.0}))
+    cal = "__amd_rocclr_copyBuffer"
+    _write_csv(f"{root}/prof_copy_fetch/copy_counter_collection.csv", hdr,
+               rows({"FETCH_SIZE": bench.COPY_CAL_BYTES / 2048}, cal))
+    _write_csv(f"{root}/prof_copy_write/copy_counter_collection.csv", hdr,
+               rows({"WRITE_SIZE": bench.COPY_CAL_BYTES / 1024}, cal))
+    _write_csv(f"{root}/prof_req_{tag}/k_counter_collection.csv", hdr,
+               rows({"TCC_EA0_RDREQ_32B_sum": 10.0, "TCC_EA0_RDREQ_64B_sum": 20.0,
+                     "TCC_EA0_RDREQ_128B_sum": 1000.0, "TCC_EA0_WRREQ_64B_sum": 3000.0}))
+    _write_csv(f"{root}/prof_wreq_{tag}/k_counter_collection.csv", hdr,
+               rows({"TCC_EA0_WRREQ_sum": 3004.0, "TCC_EA0_RDREQ_sum": 1030.0}))
+    _write_csv(f"{root}/prof_sq_{tag}/k_counter_collection.csv", hdr,
+               rows({"SQ_WAVES": 1000.0, "SQ_INSTS_VALU": 50_000.0, "SQ_INSTS_MFMA": 0.0,
+                     "SQ_ACTIVE_INST_VALU": 256 * 1000 * 0.25, "SQ_VALU_MFMA_BUSY_CYCLES": 0.0,
+                     "SQ_WAVE_CYCLES": 100.0, "SQ_WAIT_INST_ANY": 50.0, "GRBM_GUI_ACTIVE": 8000.0}))
+    out = str(tmp_path / "out")
+    path = bench.summarize(root, "decode_b256_h48_d128_t1", "f32", out_dir=out)
+    md = open(path).read()
+    assert path.endswith("gdn_decode_kernel_decode_b256_h48_d128_t1_f32.md")
+    assert "| gdn_decode_kernel | 10 | 260000 |" in md
+    # calibration: FETCH x 2 KiB, WRITE x 1 KiB
+    hbm = 400_000 * 2048 + 800_000 * 1024
+    assert f"Measured HBM bytes per launch {hbm} " in md
+    rb = 32 * 10 + 64 * 20 + 128 * 1000
+    wb = 64 * 3000 + 32 * 4
+    assert f"By request size: {rb + wb} bytes per launch" in md
+    # 50 VALU instructions per wave; VALU busy 25% of 256 CUs x 1000 cycles
+    assert "| gdn_decode_kernel | 1000 | 50.0 | 0.0 | 25.0 | 0.0 | 0.50 |" in md
+    kv = bench.read_kv(os.path.join(out, "traffic_decode_b256_h48_d128_t1_f32.txt"))
+    assert int(kv["hbm_bytes_per_launch"]) == hbm
+    assert kv["kernel_source_sha256_16"] == bench.kernel_source_hash("decode")
