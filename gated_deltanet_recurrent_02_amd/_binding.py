@@ -22,7 +22,8 @@ _CODE_DTYPE = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16, GDN_F16: torch.
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_state_alloc", "gdn_state_free", "gdn_decode_step", "gdn_decode_verify",
            "gdn_conv_gate_decode", "gdn_prefill_workspace_size", "gdn_prefill",
-           "gdn_lowrank_decode_step", "gdn_status_string", "gdn_last_error")
+           "gdn_prefill_noalloc", "gdn_lowrank_decode_step", "gdn_status_string",
+           "gdn_last_error")
 
 
 class GDNError(RuntimeError):
@@ -66,6 +67,8 @@ def _declare(L):
     L.gdn_prefill.argtypes = [i64, i32, i32, i32, i32, P, P, P, i, P, P, P, i, P, f32, P,
                               ctypes.c_size_t, P]
     L.gdn_prefill.restype = i
+    L.gdn_prefill_noalloc.argtypes = [i64, i32, i32, i32, i32, P, P, P, i, P, P, P, i, P, f32, P]
+    L.gdn_prefill_noalloc.restype = i
     L.gdn_lowrank_decode_step.argtypes = [i64, i32, i32, i32, i32, i32, P, P, P, i, P, P, P, P, i,
                                           P, P, P, f32, P]
     L.gdn_lowrank_decode_step.restype = i
@@ -168,6 +171,25 @@ def prefill(q, k, v, alpha, beta, state, o=None, scale: float = 1.0, workspace=N
     check(lib().gdn_prefill(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _DTYPE_CODE[q.dtype],
                             _ptr(alpha), _ptr(beta), _ptr(state), _DTYPE_CODE[state.dtype],
                             _ptr(o), float(scale), _ptr(workspace), nbytes, _stream(q.device)))
+    return o
+
+
+def prefill_noalloc(q, k, v, alpha, beta, state, o, scale: float = 1.0):
+    """gdn_prefill_noalloc on torch tensors: prefill() with the library's fixed device scratch
+    instead of a workspace. Allocates nothing, so `o` must be given."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", (B, T, H, dk), _ACT)
+    _need(k, "k", (B, T, H, dk), (q.dtype,))
+    _need(v, "v", (B, T, H, dv), (q.dtype,))
+    _need(alpha, "alpha", (B, T, H), (torch.float32,))
+    _need(beta, "beta", (B, T, H), (torch.float32,))
+    _need(state, "state", (B, H, dv, dk), _ACT)
+    _need(o, "o", (B, T, H, dv), (q.dtype,))
+    check(lib().gdn_prefill_noalloc(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                    _DTYPE_CODE[q.dtype], _ptr(alpha), _ptr(beta), _ptr(state),
+                                    _DTYPE_CODE[state.dtype], _ptr(o), float(scale),
+                                    _stream(q.device)))
     return o
 
 

@@ -319,13 +319,17 @@ gdn_status gdn_prefill_workspace_size(int64_t B, int32_t T, int32_t H, int32_t d
     return GDN_OK;
 }
 
-gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
-                       const void* q, const void* k, const void* v, gdn_dtype act_dtype,
-                       const float* alpha, const float* beta,
-                       void* state, gdn_dtype state_dtype,
-                       void* o, float scale, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-    static const char* fn = "gdn_prefill";
+}  // extern "C"
+
+namespace {
+
+// gdn_prefill and gdn_prefill_noalloc: validation, then the launch with the given workspace.
+// `workspace` NULL means the library's fixed device scratch (no allocation, no caller buffer).
+gdn_status prefill_impl(const char* fn, int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                        const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                        const float* alpha, const float* beta, void* state, gdn_dtype state_dtype,
+                        void* o, float scale, void* workspace, size_t workspace_bytes,
+                        bool fixed_scratch, void* stream) {
     g_last_error.clear();
     gdn_status s = check_shape(fn, B, T, H, dk, dv);
     if (s != GDN_OK) return s;
@@ -335,27 +339,46 @@ gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
     if (B * (int64_t)H * gdn::prefill_chunks(T) * gdn::kPrefillWaveThreads >= gdn::kMaxWorkItems)
         return fail(GDN_ERR_UNSUPPORTED, std::string(fn) + ": B * H * ceil(T / 16) must be < 2^26 (one dispatch)");
     s = check_ptrs(fn, {{"q", q}, {"k", k}, {"v", v}, {"alpha", alpha}, {"beta", beta},
-                        {"state", state}, {"o", o}, {"workspace", workspace}});
+                        {"state", state}, {"o", o}});
     if (s != GDN_OK) return s;
     size_t need = 0;
     if (!prefill_ws_bytes(B, T, H, &need)) return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": size overflows");
-    if (workspace_bytes < need)
-        return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": workspace has " +
-                                                  std::to_string(workspace_bytes) + " bytes, " +
-                                                  std::to_string(need) + " needed");
+    if (fixed_scratch) {
+        if (need > gdn::kPrefillScratchBytes)
+            return fail(GDN_ERR_UNSUPPORTED,
+                        std::string(fn) + ": B * H * ceil(T / 16) * 2176 = " + std::to_string(need) +
+                            " bytes of chunk records exceed the fixed scratch of " +
+                            std::to_string(gdn::kPrefillScratchBytes) +
+                            " bytes (use gdn_prefill with a workspace)");
+    } else {
+        s = check_ptrs(fn, {{"workspace", workspace}});
+        if (s != GDN_OK) return s;
+        if (workspace_bytes < need)
+            return fail(GDN_ERR_INVALID_ARGUMENT, std::string(fn) + ": workspace has " +
+                                                      std::to_string(workspace_bytes) + " bytes, " +
+                                                      std::to_string(need) + " needed");
+    }
     const size_t tokens = (size_t)B * T * H;
     const size_t ab = dtype_bytes(act_dtype);
     const size_t state_bytes = (size_t)B * H * dk * dv * dtype_bytes(state_dtype);
     const Range r_q = range("q", q, tokens * dk * ab), r_k = range("k", k, tokens * dk * ab);
     const Range r_v = range("v", v, tokens * dv * ab), r_a = range("alpha", alpha, tokens * 4);
     const Range r_b = range("beta", beta, tokens * 4), r_s = range("state", state, state_bytes);
-    const Range r_o = range("o", o, tokens * dv * ab), r_w = range("workspace", workspace, need);
-    s = check_disjoint(fn, r_o, {r_q, r_k, r_v, r_a, r_b, r_s, r_w});
-    if (s != GDN_OK) return s;
-    s = check_disjoint(fn, r_s, {r_q, r_k, r_v, r_a, r_b, r_w});
-    if (s != GDN_OK) return s;
-    s = check_disjoint(fn, r_w, {r_q, r_k, r_v, r_a, r_b});
-    if (s != GDN_OK) return s;
+    const Range r_o = range("o", o, tokens * dv * ab);
+    if (fixed_scratch) {
+        s = check_disjoint(fn, r_o, {r_q, r_k, r_v, r_a, r_b, r_s});
+        if (s != GDN_OK) return s;
+        s = check_disjoint(fn, r_s, {r_q, r_k, r_v, r_a, r_b});
+        if (s != GDN_OK) return s;
+    } else {
+        const Range r_w = range("workspace", workspace, need);
+        s = check_disjoint(fn, r_o, {r_q, r_k, r_v, r_a, r_b, r_s, r_w});
+        if (s != GDN_OK) return s;
+        s = check_disjoint(fn, r_s, {r_q, r_k, r_v, r_a, r_b, r_w});
+        if (s != GDN_OK) return s;
+        s = check_disjoint(fn, r_w, {r_q, r_k, r_v, r_a, r_b});
+        if (s != GDN_OK) return s;
+    }
 
     gdn::PrefillArgs a;
     a.B = B; a.T = T; a.H = H; a.D = dk;
@@ -363,10 +386,40 @@ gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
     a.alpha = alpha; a.beta = beta;
     a.state = state; a.state_dtype = to_dtype(state_dtype);
     a.o = o; a.scale = scale;
-    a.ws = static_cast<float*>(workspace);
+    if (fixed_scratch) {
+        float* p = nullptr;
+        hipError_t e = gdn::prefill_scratch_address(&p);
+        if (e != hipSuccess) return fail_hip((std::string(fn) + ": scratch address").c_str(), e);
+        a.ws = p;
+    } else {
+        a.ws = static_cast<float*>(workspace);
+    }
     hipError_t e = gdn::launch_prefill(a, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail_hip("gdn_prefill: kernel launch", e);
+    if (e != hipSuccess) return fail_hip((std::string(fn) + ": kernel launch").c_str(), e);
     return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                       const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                       const float* alpha, const float* beta,
+                       void* state, gdn_dtype state_dtype,
+                       void* o, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    return prefill_impl("gdn_prefill", B, T, H, dk, dv, q, k, v, act_dtype, alpha, beta, state,
+                        state_dtype, o, scale, workspace, workspace_bytes, false, stream);
+}
+
+gdn_status gdn_prefill_noalloc(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                               const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                               const float* alpha, const float* beta,
+                               void* state, gdn_dtype state_dtype,
+                               void* o, float scale, void* stream) {
+    return prefill_impl("gdn_prefill_noalloc", B, T, H, dk, dv, q, k, v, act_dtype, alpha, beta,
+                        state, state_dtype, o, scale, nullptr, 0, true, stream);
 }
 
 gdn_status gdn_lowrank_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,

@@ -43,6 +43,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_prefill_launch.h"
@@ -641,6 +643,41 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
         case 64: return launch_prefill_d<64>(a, s);
         default: return launch_prefill_d<128>(a, s);
     }
+}
+
+// ------------------------------------------------------------------------ fixed scratch
+
+// The chunk records of gdn_prefill_noalloc live in this file-scope device array instead of a
+// caller's workspace. Every GPU the library runs on holds its own copy until the process ends;
+// in host code `scratch` is only a host-side stand-in for it, so its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current) and only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kPrefillScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t prefill_scratch_address(float** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = static_cast<float*>(p);
+    return hipSuccess;
 }
 
 }  // namespace gdn

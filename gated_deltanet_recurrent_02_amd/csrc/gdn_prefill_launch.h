@@ -44,4 +44,12 @@ inline int64_t prefill_chunks(int32_t T) { return (T + kPrefillChunk - 1) / kPre
 // Enqueues the prep kernel, then the state kernel; nothing is synchronised.
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// Size of the fixed device scratch of gdn_prefill_noalloc: 64 MiB, i.e. records for
+// B * H * ceil(T / 16) <= 30840 (head, chunk) pairs (one 48-head sequence of 10,280 tokens).
+constexpr size_t kPrefillScratchBytes = size_t(64) << 20;
+
+// Device address of the current device's copy of that scratch (looked up on the first call on
+// each device, cached afterwards; thread-safe). Allocates nothing.
+hipError_t prefill_scratch_address(float** out);
+
 }  // namespace gdn

@@ -17,7 +17,8 @@
  * Conventions shared by every entry point:
  *  - Buffers. Every tensor is dense, row-major (last index fastest) and lives in device memory
  *    of the current HIP device. The caller owns every buffer; the library keeps no pointer
- *    after a call returns and holds no global state besides a thread-local error string.
+ *    after a call returns and holds no global state besides a thread-local error string and
+ *    the fixed device scratch of gdn_prefill_noalloc.
  *  - Alignment. Every device pointer must be 16-byte aligned.
  *  - Streams. `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
  *    enqueued asynchronously: no host synchronisation, no allocation, no environment reads.
@@ -203,6 +204,27 @@ gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                        void* state, gdn_dtype state_dtype,
                        void* o, float scale, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * gdn_prefill_noalloc — gdn_prefill for callers that cannot allocate or pass device memory of
+ * their own: code being captured into a HIP graph, tight serving loops, and harnesses that
+ * forbid allocation. Same arguments, results and errors as gdn_prefill, minus the workspace:
+ * the chunk records go to a fixed scratch array that the library holds in device memory, 64 MiB
+ * per GPU it runs on, for the life of the process. The call allocates nothing and calls no
+ * allocating routine; the first call on each device looks the array's address up (make that
+ * first call outside graph capture).
+ * Limit: B * H * ceil(T / 16) * 2176 <= 67,108,864 bytes (30,840 head-chunks, e.g. one 48-head
+ * sequence of up to 10,280 tokens); larger calls return GDN_ERR_UNSUPPORTED and enqueue
+ * nothing (use gdn_prefill with a workspace). Every call on one GPU shares that GPU's array:
+ * calls on one stream are ordered and safe; two calls in flight at once on one GPU (different
+ * streams) race on it. The array's contents on entry do not matter (the prep kernel writes
+ * every record the state kernel reads).
+ */
+gdn_status gdn_prefill_noalloc(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                               const void* q, const void* k, const void* v, gdn_dtype act_dtype,
+                               const float* alpha, const float* beta,
+                               void* state, gdn_dtype state_dtype,
+                               void* o, float scale, void* stream);
 
 /*
  * gdn_lowrank_decode_step — T tokens of the recurrence on a sliding-window low-rank state, the

@@ -10,4 +10,5 @@ hipError_t launch_verify(const VerifyArgs&, hipStream_t) { return hipErrorNoDevi
 hipError_t launch_conv_gate_decode(const FusedArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_lowrank(const LowrankArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t prefill_scratch_address(float**) { return hipErrorNoDevice; }
 }

@@ -287,6 +287,48 @@ def test_prefill_empty_work_and_valid_call_without_device():
     assert "kernel launch" in last_error()
 
 
+def prefill_noalloc(B=2, T=40, H=4, D=16, q=None, o=None, state=None, act=F32):
+    """gdn_prefill_noalloc with disjoint fake buffers."""
+    q = P(0) if q is None else q
+    state = P(80 * MB) if state is None else state
+    o = P(160 * MB) if o is None else o
+    return gdn.lib().gdn_prefill_noalloc(B, T, H, D, D, q, P(16 * MB), P(32 * MB), act, P(48 * MB),
+                                         P(64 * MB), state, F32, o, 1.0, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H=0), INVALID, "H must be"),
+    (dict(D=96), UNSUPPORTED, "head dims"),
+    (dict(act=9), INVALID, "dtype"),
+    (dict(q=ctypes.c_void_p(0)), INVALID, "q is NULL"),
+    (dict(o=P(80 * MB)), INVALID, "o overlaps state"),
+    (dict(state=P(16 * MB)), INVALID, "state overlaps k"),
+    # 48 heads x 650 chunks x 2176 bytes = 67,891,200 > 64 MiB of fixed scratch
+    (dict(B=1, H=48, T=10400, D=128), UNSUPPORTED, "exceed the fixed scratch"),
+    (dict(B=4, H=48, T=4096, D=128), UNSUPPORTED, "exceed the fixed scratch"),
+])
+@fake_ptrs
+def test_prefill_noalloc_rejects(kw, status, msg):
+    assert prefill_noalloc(**kw) == status
+    assert msg in last_error()
+
+
+@fake_ptrs
+def test_prefill_noalloc_empty_work_and_valid_calls_without_device():
+    N = ctypes.c_void_p(0)
+    L = gdn.lib()
+    assert L.gdn_prefill_noalloc(0, 16, 4, 16, 16, N, N, N, F32, N, N, N, F32, N, 1.0, None) == 0
+    assert L.gdn_prefill_noalloc(2, 0, 4, 16, 16, N, N, N, F32, N, N, N, F32, N, 1.0, None) == 0
+    # within the limit (the largest call that fits: 30,840 records of 2176 bytes <= 64 MiB);
+    # validation passes and the call fails only where it needs the device
+    assert prefill_noalloc() == HIP
+    GB = 1 << 30
+    assert L.gdn_prefill_noalloc(1, 514 * 16, 60, 128, 128, P(0), P(GB), P(2 * GB), F32,
+                                 P(3 * GB), P(3 * GB + 4 * MB), P(4 * GB), F32, P(5 * GB), 1.0,
+                                 None) == HIP
+    assert "gdn_prefill_noalloc" in last_error()
+
+
 def lowrank(B=2, T=2, H=4, D=16, r=16, q=None, k=None, v=None, act=F32, alpha=None, beta=None,
             U=None, K=None, sdt=F32, c=None, pos=None, o=None):
     """gdn_lowrank_decode_step with disjoint fake buffers unless a pointer is given."""
