@@ -190,14 +190,14 @@ __device__ __forceinline__ void gstore(void* p, const Words<NBYTES>& r) {
 
 // A kernel instance: head dim D, state type ST, WAVES wave64s per workgroup, SPLIT workgroups
 // per head (each owning D/SPLIT consecutive rows), TCH tokens staged in LDS per round,
-// nontemporal state loads (NTL) / stores (NTS), the tile order over XCDs (XCD, see
-// tile_index), and LPR lanes per state row.
+// nontemporal state loads (NTL) / stores (NTS), the tile order over XCDs (GRP consecutive
+// tiles per XCD, see tile_index), and LPR lanes per state row.
 template <int D_, typename ST_, int WAVES_, int SPLIT_, int TCH_, bool NTL_, bool NTS_,
-          int XCD_ = 0, int LPR_ = 16>
+          int GRP_ = 1, int LPR_ = 16>
 struct Geo {
     static constexpr int D = D_;
     using ST = ST_;
-    static constexpr int WAVES = WAVES_, SPLIT = SPLIT_, TCH = TCH_, XCD = XCD_, LPR = LPR_;
+    static constexpr int WAVES = WAVES_, SPLIT = SPLIT_, TCH = TCH_, GRP = GRP_, LPR = LPR_;
     static constexpr bool NTL = NTL_, NTS = NTS_;
     static constexpr int E = D / LPR;                        // state columns per lane
     static constexpr int ES = (int)sizeof(ST);               // bytes per state element
@@ -214,6 +214,7 @@ struct Geo {
     static_assert(D % SPLIT == 0 && RPG % WAVES == 0, "bad split");
     static_assert(RPW % RPP == 0 && P >= 1 && P <= LPR, "bad wave count");
     static_assert(TCH >= 1, "bad token chunk");
+    static_assert(GRP >= 1, "bad tile group");
     // Column held by lane l (0..LPR-1 within its row group) as its element e.
     static __device__ __forceinline__ int col(int l, int e) {
         return (e / VW) * (LPR * VW) + l * VW + (e % VW);
@@ -221,25 +222,20 @@ struct Geo {
 };
 
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on XCD i % 8), and
-// each XCD has its own L2. The tile order decides which tiles share an L2:
-//   XCD 0: tile = workgroup index (consecutive tiles on different XCDs);
-//   XCD 1: each XCD walks one contiguous range of tiles;
-//   XCD 2: the SPLIT tiles of a head stay on one XCD (its q, k, v are fetched into one L2),
-//          consecutive heads go to consecutive XCDs; heads past the last multiple of 8 keep
-//          the plain order.
-// Each map is a bijection of [0, n) for n = gridDim.x.
-template <int XCD, int SPLIT>
+// each XCD has its own L2. The tile order decides which tiles share an L2: runs of GRP
+// consecutive tiles go to one XCD, consecutive runs to consecutive XCDs. GRP = 1 is the plain
+// order (consecutive tiles on different XCDs); GRP = SPLIT keeps all tiles of a head on one XCD
+// (its q, k and v are fetched into one L2). Tiles past the last multiple of 8 * GRP keep the
+// plain order. The map is a bijection of [0, n) for n = gridDim.x.
+template <int GRP>
 __device__ __forceinline__ uint32_t tile_index(uint32_t bid, uint32_t n) {
-    if constexpr (XCD == 1) {
-        const uint32_t x = bid & 7u, i = bid >> 3, q = n >> 3, r = n & 7u;
-        return x * q + min(x, r) + i;
-    } else if constexpr (XCD == 2) {
-        const uint32_t grouped = (n / (8u * SPLIT)) * (8u * SPLIT);
+    if constexpr (GRP == 1) {
+        return bid;
+    } else {
+        const uint32_t grouped = (n / (8u * GRP)) * (8u * GRP);
         if (bid >= grouped) return bid;
         const uint32_t x = bid & 7u, i = bid >> 3;
-        return ((i / SPLIT) * 8u + x) * SPLIT + (i % SPLIT);
-    } else {
-        return bid;
+        return ((i / GRP) * 8u + x) * GRP + (i % GRP);
     }
 }
 
@@ -613,7 +609,7 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     __shared__ TokLds<D, G::TCH> L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane / G::LPR, l = lane % G::LPR;
-    const uint32_t tile = tile_index<G::XCD, G::SPLIT>(blockIdx.x, gridDim.x);
+    const uint32_t tile = tile_index<G::GRP>(blockIdx.x, gridDim.x);
     const int64_t n = tile / G::SPLIT;  // b * H + h
     const int part = (int)(tile - n * G::SPLIT);
     const int64_t b = n / H;
@@ -624,16 +620,21 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     float S[G::P][G::E];
     float c = 1.0f;
     if constexpr (G::TCH == 1) {
-        // One token per round (the one-token launch shape): stage q, k, v element by element
-        // after the state loads are issued. Measured on MI355X at B=256 H=48 D=128 T=1, this
-        // exact form (vector loads of alpha and beta by the lanes below nt) beats a 16-byte
-        // fetch issued before or after the state loads, and a scalar-load variant, by 1-3%.
+        // One token per round (the one-token launch shape): stage q, k and the workgroup's own
+        // v rows element by element after the state loads are issued. Measured on MI355X at
+        // B=256 H=48 D=128 T=1, this form (vector loads of alpha and beta by the lanes below
+        // nt) beats a 16-byte fetch issued before or after the state loads, and a scalar-load
+        // variant, by 1-3%; staging only the own v rows instead of all of v: 256.3 -> 253.2 us.
         load_state<G>(Sg, rbase + g, l, S);
         for (int t0 = 0; t0 < T; t0 += G::TCH) {
             const int nt = min(G::TCH, T - t0);
             if (t0 > 0) __syncthreads();  // the previous round's readers are done with L
-            for (int i = tid; i < nt * 3 * D; i += G::NT) {
-                const int tt = i / (3 * D), r = i - tt * 3 * D, which = r / D, j = r - which * D;
+            // q and k in full, v for the workgroup's own rows only
+            constexpr int NE = 2 * D + G::RPG;  // elements staged per token
+            for (int i = tid; i < nt * NE; i += G::NT) {
+                const int tt = i / NE, r = i - tt * NE;
+                const int which = r < D ? 0 : (r < 2 * D ? 1 : 2);
+                const int j = which == 2 ? part * G::RPG + (r - 2 * D) : r - which * D;
                 const size_t tok = ((size_t)b * T + t0 + tt) * H + h;
                 const AT* src = which == 0 ? q : (which == 1 ? k : v);
                 const float x = act_to_f32(src[tok * D + j]);
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(G::NT) void gdn_verify_kernel(
     __shared__ TokLds<D, G::TCH> L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane / G::LPR, l = lane % G::LPR;
-    const uint32_t tile = tile_index<G::XCD, G::SPLIT>(blockIdx.x, gridDim.x);
+    const uint32_t tile = tile_index<G::GRP>(blockIdx.x, gridDim.x);
     const int64_t n = tile / G::SPLIT;  // b * H + h
     const int part = (int)(tile - n * G::SPLIT);
     const int64_t b = n / H;
@@ -790,7 +791,7 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
     __shared__ TokLds<D, G::TCH> L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane / G::LPR, l = lane % G::LPR;
-    const uint32_t tile = tile_index<G::XCD, 1>(blockIdx.x, gridDim.x);
+    const uint32_t tile = tile_index<G::GRP>(blockIdx.x, gridDim.x);
     const int64_t n = tile;
     const int64_t b = n / H;
     const int h = (int)(n - b * H);
@@ -977,10 +978,14 @@ constexpr int64_t kOneTokenSpreadHeads = 8192;
 //    state loads and stores -- 79% of HBM peak; larger workgroups synchronise their waves'
 //    load/store phases and lose 5-15%; 16 rows per wave (256 -> 278 us at B = 256) and 4 rows
 //    per wave (-> 294 us) lose too;
+//    From 8192 heads, runs of 4 consecutive tiles share an XCD (a head's 16 tiles on 4 XCDs):
+//    at B = 256 H = 48, 253.1 -> 251.6 us against consecutive tiles on different XCDs, and
+//    runs of 2, 8 and 16 tiles measured 260.4, 263.4 and 259.5 us (an in-place stream with
+//    the same tiles and no arithmetic shows the same order: the state stream's placement over
+//    the XCDs decides, not the q, k, v fetches the grouping saves).
 //    Below 8192 heads the 16 tiles of a head stay on one XCD (its q, k and v are fetched into
 //    one L2): B = 8 .. 128 at H = 48 run 3-8% faster that way (B = 64: 70.4 -> 65.8 us),
-//    B = 160 and 192 tie, and B = 256 is 2% slower than with consecutive tiles on different
-//    XCDs, which it keeps;
+//    B = 160 and 192 tie;
 //  * one token, bf16 state: all rows of a head in one workgroup, 8 rows per wave, 8 lanes per
 //    row (two 16-byte loads per lane and row): 140 -> 130 us at B=256 H=48 D=128 against 16
 //    lanes per row (fp32 states show no difference);
@@ -996,32 +1001,32 @@ constexpr int64_t kOneTokenSpreadHeads = 8192;
 //    it. The fused kernel needs the whole head in one workgroup (the conv state of the q and
 //    k channels is read and rewritten by it).
 template <int D, typename ST> struct DecodeOneToken {  // 2-byte states
-    using G = Geo<D, ST, D / 8, 1, 1, true, true, 0, 8>;
+    using G = Geo<D, ST, D / 8, 1, 1, true, true, 1, 8>;
 };
 template <int D> struct DecodeOneToken<D, float> {
-    using G = Geo<D, float, 1, D / 8, 1, true, true>;
-    using G_small = Geo<D, float, 1, D / 8, 1, true, true, 2>;  // fewer than 8192 heads
+    using G = Geo<D, float, 1, D / 8, 1, true, true, 4>;
+    using G_small = Geo<D, float, 1, D / 8, 1, true, true, D / 8>;  // fewer than 8192 heads
 };
 
 template <int D, typename ST> struct DecodeTokens {  // 2-byte states
-    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 1, 8>;
 };
 template <int D> struct DecodeTokens<D, float> {
-    using G = Geo<D, float, 1, max_int(1, D / 16), 8, true, true, 2, 16>;
+    using G = Geo<D, float, 1, max_int(1, D / 16), 8, true, true, max_int(1, D / 16), 16>;
 };
 
 template <int D, typename ST> struct VerifyTokens {  // 2-byte states
-    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 1, 8>;
 };
 template <int D> struct VerifyTokens<D, float> {
-    using G = Geo<D, float, max_int(1, D / 16), 1, 8, true, true, 0, 16>;
+    using G = Geo<D, float, max_int(1, D / 16), 1, 8, true, true, 1, 16>;
 };
 
 template <int D, typename ST> struct FusedTokens {  // 2-byte states
-    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 0, 8>;
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 1, 8>;
 };
 template <int D> struct FusedTokens<D, float> {
-    using G = Geo<D, float, max_int(1, D / 32), 1, 8, true, true, 0, 8>;
+    using G = Geo<D, float, max_int(1, D / 32), 1, 8, true, true, 1, 8>;
 };
 
 template <int D, typename ST, typename AT>
