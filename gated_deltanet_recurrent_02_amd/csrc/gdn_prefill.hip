@@ -528,6 +528,203 @@ __device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
         }
 }
 
+// Two consecutive chunks (x0 = chunk ci, x1 = chunk ci + 1) from one split of S', for the
+// bf16 matrix-core path. With S_mid = gamma0_15 c S' + K0^T diag(Gam_end0) Delta0 the state
+// between the chunks (never formed) and M = K1 K0^T, N = Q1 K0^T (16 x 16), the second chunk's
+// products are
+//     K1 S_mid^T = c_mid K1 S'^T + (M diag(Gam_end0)) Delta0,   c_mid = gamma0_15 c,
+//     Q1 S_mid^T = c_mid Q1 S'^T + (N diag(Gam_end0)) Delta0,
+// so both chunks take their products from the same three bf16 parts of S' and the second adds
+// a 16 x 16 correction on the matrix cores. The state update then runs once for both chunks,
+// contracting over their 32 tokens on the 16 x 16 x 32 form:
+//     S'_end = S' + K0^T diag(Gam_end0 gamma1_15 / c_end) Delta0 + K1^T diag(Gam_end1 / c_end) Delta1,
+// c_end = gamma1_15 c_mid (folded into S' when out of [2^-64, 2^64], as in chunk_step). Same
+// algebra as two chunk_step calls; fp32 rounding differs. `prefetch` is called once the S'
+// products are done (it issues the next pair's loads into registers those products freed).
+template <int D, int RT, typename AT, typename F>
+__device__ __forceinline__ void pair_step(f32x4 (&S)[RT][D / 16], float& c,
+                                          const ChunkOps<D, RT, AT>& x0,
+                                          const ChunkOps<D, RT, AT>& x1, int ci, int T, int H,
+                                          int64_t b, int h, int row0, AT* __restrict__ o,
+                                          float scale, int g, F&& prefetch) {
+    static_assert(kBf16Mma<D, AT>, "the paired form runs on the bf16 matrix cores");
+    constexpr int NMT = D / 16;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 X0[RT], Y0[RT], X1[RT], Y1[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) X0[r] = Y0[r] = X1[r] = Y1[r] = zero4;
+    // QKj: lane (g, m) ends with k_{4g+s} . q_m of chunk j (P's a operand); M and N: lane
+    // (g, n) ends with k0_{4g+s} . k1_n and k0_{4g+s} . q1_n, i.e. M[n][4g+s], N[n][4g+s], the
+    // a operands of the corrections.
+    f32x4 QK0 = zero4, QK1 = zero4, M = zero4, N = zero4;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+        const u32x4 ka0 = {x0.kx.w[4 * s], x0.kx.w[4 * s + 1], x0.kx.w[4 * s + 2], x0.kx.w[4 * s + 3]};
+        const u32x4 qa0 = {x0.qx.w[4 * s], x0.qx.w[4 * s + 1], x0.qx.w[4 * s + 2], x0.qx.w[4 * s + 3]};
+        const u32x4 ka1 = {x1.kx.w[4 * s], x1.kx.w[4 * s + 1], x1.kx.w[4 * s + 2], x1.kx.w[4 * s + 3]};
+        const u32x4 qa1 = {x1.qx.w[4 * s], x1.qx.w[4 * s + 1], x1.qx.w[4 * s + 2], x1.qx.w[4 * s + 3]};
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            Split3 p[4];
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int t = 8 * s + 2 * pp;
+                p[pp] = split3(S[r][t % NMT][t / NMT], S[r][t % NMT + 1][t / NMT]);
+            }
+            const u32x4 bh = {p[0].h, p[1].h, p[2].h, p[3].h};
+            const u32x4 bm = {p[0].m, p[1].m, p[2].m, p[3].m};
+            const u32x4 bl = {p[0].l, p[1].l, p[2].l, p[3].l};
+            X0[r] = mfma_k32(ka0, bh, X0[r]);
+            X1[r] = mfma_k32(ka1, bh, X1[r]);
+            Y0[r] = mfma_k32(qa0, bh, Y0[r]);
+            Y1[r] = mfma_k32(qa1, bh, Y1[r]);
+            X0[r] = mfma_k32(ka0, bm, X0[r]);
+            X1[r] = mfma_k32(ka1, bm, X1[r]);
+            Y0[r] = mfma_k32(qa0, bm, Y0[r]);
+            Y1[r] = mfma_k32(qa1, bm, Y1[r]);
+            X0[r] = mfma_k32(ka0, bl, X0[r]);
+            X1[r] = mfma_k32(ka1, bl, X1[r]);
+        }
+        QK0 = mfma_k32(ka0, qa0, QK0);
+        QK1 = mfma_k32(ka1, qa1, QK1);
+        M = mfma_k32(ka0, ka1, M);
+        N = mfma_k32(ka0, qa1, N);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // First chunk, as in chunk_step.
+    f32x4 Z0[RT], D0[RT], O0[RT];
+    f32x4 gx0, gy0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        gx0[j] = x0.gm[j] * c;
+        gy0[j] = gx0[j] * scale;
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        D0[r] = zero4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            Z0[r][j] = (4 * g + j < x0.nv) ? fmaf(-gx0[j], X0[r][j], to_f32<AT>(x0.v[r][j])) : 0.0f;
+            O0[r][j] = gy0[j] * Y0[r][j];
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) D0[r] = mfma4(x0.tb[s], Z0[r][s], D0[r]);
+    const f32x4 pm0 = x0.pm * QK0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) O0[r] = mfma4(pm0[s], D0[r][s], O0[r]);
+
+    // Second chunk: its products with S_mid, the corrections through Delta0.
+    const float cm = x0.gend * c;
+    const f32x4 Mg = M * x0.ge, Ng = N * x0.ge;
+    f32x4 Xc[RT], Yc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) Xc[r] = Yc[r] = zero4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            Xc[r] = mfma4(Mg[s], D0[r][s], Xc[r]);
+            Yc[r] = mfma4(Ng[s], D0[r][s], Yc[r]);
+        }
+    f32x4 Z1[RT], D1[RT], O1[RT];
+    f32x4 gx1, gy1, sg1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        gx1[j] = x1.gm[j] * cm;
+        gy1[j] = gx1[j] * scale;
+        sg1[j] = x1.gm[j] * scale;
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        D1[r] = zero4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float z = fmaf(-gx1[j], X1[r][j], to_f32<AT>(x1.v[r][j]));
+            Z1[r][j] = (4 * g + j < x1.nv) ? fmaf(-x1.gm[j], Xc[r][j], z) : 0.0f;
+            O1[r][j] = fmaf(gy1[j], Y1[r][j], sg1[j] * Yc[r][j]);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) D1[r] = mfma4(x1.tb[s], Z1[r][s], D1[r]);
+    const f32x4 pm1 = x1.pm * QK1;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) O1[r] = mfma4(pm1[s], D1[r][s], O1[r]);
+
+    // The update over both chunks' 32 tokens.
+    float cn = x1.gend * cm;
+    if (!(fabsf(cn) >= 0x1p-64f && fabsf(cn) <= 0x1p64f)) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) S[r][mt] *= cn;
+        cn = 1.0f;
+    }
+    c = cn;
+    const float rc = 1.0f / cn;
+    const float r0 = x1.gend * rc;
+    u32x4 dh[RT], dm[RT], dl[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        f32x4 t0, t1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            t0[j] = (x0.ge[j] * r0) * D0[r][j];
+            t1[j] = (x1.ge[j] * rc) * D1[r][j];
+        }
+        const Split3 p0 = split3(t0[0], t0[1]), p1 = split3(t0[2], t0[3]);
+        const Split3 p2 = split3(t1[0], t1[1]), p3 = split3(t1[2], t1[3]);
+        dh[r] = u32x4{p0.h, p1.h, p2.h, p3.h};
+        dm[r] = u32x4{p0.m, p1.m, p2.m, p3.m};
+        dl[r] = u32x4{p0.l, p1.l, p2.l, p3.l};
+    }
+    // 16 x 16 x 32: lane group g holds contraction slots 8g .. 8g+7 = tokens 4g .. 4g+3 of the
+    // first chunk, then of the second; K^T as packed pairs of those tokens of column NMT m + mt.
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+        const int wi = mt >> 1;
+        const uint32_t a0 = x0.ku[0].w[wi], a1 = x0.ku[1].w[wi], a2 = x0.ku[2].w[wi], a3 = x0.ku[3].w[wi];
+        const uint32_t b0 = x1.ku[0].w[wi], b1 = x1.ku[1].w[wi], b2 = x1.ku[2].w[wi], b3 = x1.ku[3].w[wi];
+        const u32x4 ka = (mt & 1)
+            ? u32x4{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u),
+                    (b0 >> 16) | (b1 & 0xffff0000u), (b2 >> 16) | (b3 & 0xffff0000u)}
+            : u32x4{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16),
+                    (b0 & 0xffffu) | (b1 << 16), (b2 & 0xffffu) | (b3 << 16)};
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            S[r][mt] = mfma_k32(ka, dh[r], S[r][mt]);
+            S[r][mt] = mfma_k32(ka, dm[r], S[r][mt]);
+            S[r][mt] = mfma_k32(ka, dl[r], S[r][mt]);
+        }
+    }
+
+    const int64_t tok0 = (b * T + ci * CH) * H + h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        AT* ot = o + (tok0 + (int64_t)(4 * g + j) * H) * D + row0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) ot[16 * r] = from_f32<AT>(O0[r][j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (4 * g + j < x1.nv) {
+            AT* ot = o + (tok0 + (int64_t)(CH + 4 * g + j) * H) * D + row0;
+#pragma unroll
+            for (int r = 0; r < RT; ++r) ot[16 * r] = from_f32<AT>(O1[r][j]);
+        }
+}
+
 // One wave per (b, h, RT tiles of 16 state rows). With `remap`, workgroup ids are regrouped so
 // the waves of a head run on one XCD (workgroup i runs on XCD i % 8) and share its L2 for the
 // head's k, q and chunk records.
@@ -562,19 +759,43 @@ __global__ __launch_bounds__(64) void gdn_prefill_state_kernel(
 
     const float* wsh = ws + (size_t)bh * nch * REC;
     float cs = 1.0f;  // S = cs S' (wave-uniform)
-    ChunkOps<D, RT, AT> A, Bo;
-    load_chunk<D, RT, AT>(A, 0, T, H, b, h, row0, q, k, v, wsh, g, n);
-    // The prefetches are unconditional (the last chunk is read again at the end): a load that
-    // only some paths issue would make the compiler wait for every load in flight. The
-    // scheduling barriers keep them ahead of the chunk's products instead of sunk to its end.
-    for (int c = 0; c < nch; c += 2) {
-        load_chunk<D, RT, AT>(Bo, min(c + 1, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
-        __builtin_amdgcn_sched_barrier(0);
-        chunk_step<D, RT, AT>(S, cs, A, c, T, H, b, h, row0, o, scale, g);
-        if (c + 1 >= nch) break;
-        load_chunk<D, RT, AT>(A, min(c + 2, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
-        __builtin_amdgcn_sched_barrier(0);
-        chunk_step<D, RT, AT>(S, cs, Bo, c + 1, T, H, b, h, row0, o, scale, g);
+    if constexpr (kBf16Mma<D, AT>) {
+        // Chunks in pairs (pair_step); the next pair's operands load while the current pair
+        // computes, issued once its S' products have freed their registers. An odd last chunk
+        // runs alone.
+        ChunkOps<D, RT, AT> A0, A1, B0, B1;
+        load_chunk<D, RT, AT>(A0, 0, T, H, b, h, row0, q, k, v, wsh, g, n);
+        load_chunk<D, RT, AT>(A1, min(1, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+        for (int c = 0; c + 1 < nch; c += 4) {
+            pair_step<D, RT, AT>(S, cs, A0, A1, c, T, H, b, h, row0, o, scale, g, [&]() {
+                load_chunk<D, RT, AT>(B0, min(c + 2, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+                load_chunk<D, RT, AT>(B1, min(c + 3, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+            });
+            if (c + 3 >= nch) break;
+            pair_step<D, RT, AT>(S, cs, B0, B1, c + 2, T, H, b, h, row0, o, scale, g, [&]() {
+                load_chunk<D, RT, AT>(A0, min(c + 4, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+                load_chunk<D, RT, AT>(A1, min(c + 5, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+            });
+        }
+        if (nch & 1) {
+            load_chunk<D, RT, AT>(A0, nch - 1, T, H, b, h, row0, q, k, v, wsh, g, n);
+            chunk_step<D, RT, AT>(S, cs, A0, nch - 1, T, H, b, h, row0, o, scale, g);
+        }
+    } else {
+        ChunkOps<D, RT, AT> A, Bo;
+        load_chunk<D, RT, AT>(A, 0, T, H, b, h, row0, q, k, v, wsh, g, n);
+        // The prefetches are unconditional (the last chunk is read again at the end): a load
+        // that only some paths issue would make the compiler wait for every load in flight. The
+        // scheduling barriers keep them ahead of the chunk's products instead of sunk to its end.
+        for (int c = 0; c < nch; c += 2) {
+            load_chunk<D, RT, AT>(Bo, min(c + 1, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+            __builtin_amdgcn_sched_barrier(0);
+            chunk_step<D, RT, AT>(S, cs, A, c, T, H, b, h, row0, o, scale, g);
+            if (c + 1 >= nch) break;
+            load_chunk<D, RT, AT>(A, min(c + 2, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
+            __builtin_amdgcn_sched_barrier(0);
+            chunk_step<D, RT, AT>(S, cs, Bo, c + 1, T, H, b, h, row0, o, scale, g);
+        }
     }
 
 #pragma unroll

@@ -2,8 +2,10 @@
 
 The oracle is the plain recurrence token by token (oracle_gdn_decode); the chunked form must
 reach the same state and outputs within the floating-point bars of parity.py. Small shapes are
-compared on every head, with ragged last chunks (T not a multiple of 16) and several chunks;
-the prompt workload (B=4, H=48, D=128, T=4096) on sampled heads.
+compared on every head, with ragged last chunks (T not a multiple of 16) and several chunks
+(bf16 activations take the chunks in pairs: even and odd chunk counts, a ragged second chunk
+of a pair and a ragged lone last chunk are all covered); the prompt workload (B=4, H=48, D=128,
+T=4096) on every head.
 """
 import numpy as np
 import pytest
@@ -33,7 +35,8 @@ def gpu_prefill(x, scale=1.0, workspace=None):
 
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("act", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("B,H,T", [(2, 3, 1), (1, 2, 16), (3, 2, 37), (1, 3, 100)])
+@pytest.mark.parametrize("B,H,T", [(2, 3, 1), (1, 2, 16), (2, 2, 20), (3, 2, 37), (2, 2, 60),
+                                   (1, 3, 100)])
 def test_small_shapes_full_compare(D, act, B, H, T):
     _announce(f"prefill B={B} H={H} D={D} T={T} act={act} state=f32")
     x = synth.decode_inputs(B, H, D, T, act=act, alpha_shift=-2.0, state_std=0.3, seed=D + T)
@@ -84,11 +87,12 @@ def test_agrees_with_decode_step():
     check_state(f64(S_p), f64(g["state"]), torch.float32)
 
 
-def test_gate_edge_values():
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_gate_edge_values(act):
     # alpha = 0 wipes the state at that token (the products of alphas carry the exact zero);
     # beta = 0 leaves a token without a write; a zero key writes nothing.
-    _announce("prefill gate edge values")
-    x = synth.decode_inputs(2, 3, 64, 50, act="f32", alpha_shift=-2.0, state_std=0.3, seed=3)
+    _announce(f"prefill gate edge values act={act}")
+    x = synth.decode_inputs(2, 3, 64, 50, act=act, alpha_shift=-2.0, state_std=0.3, seed=3)
     x["alpha"][0, 7, :] = 0.0
     x["alpha"][1, 16, 1] = 0.0      # first token of the second chunk
     x["alpha"][1, 31, 2] = 0.0      # last token of the second chunk
@@ -98,7 +102,7 @@ def test_gate_edge_values():
     S, o = gpu_prefill(x, scale=0.5)
     S_ref, o_ref = oracle_decode(x, scale=0.5)
     check_state(f64(S), S_ref, torch.float32)
-    check_o(f64(o), o_ref, torch.float32)
+    check_o(f64(o), o_ref, DT[act])
 
 
 def test_workspace_contents_do_not_matter():
@@ -146,13 +150,14 @@ def test_split_calls_continue_the_state():
     check_o(np.concatenate([f64(o1), f64(o2)], axis=1), o_ref, torch.float32)
 
 
-def test_decay_fold_paths():
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_decay_fold_paths(act):
     # The kernel keeps S / c in registers with c the running product of chunk decays and folds
     # c into the state when it leaves [2^-64, 2^64]: alpha > 1 (c grows past 2^64 within a few
     # chunks), alpha < 0 (c changes sign: folded every chunk), tiny alphas (c underflows), and
     # exact zeros mid-chunk, each on its own head.
-    _announce("prefill decay fold paths")
-    x = synth.decode_inputs(1, 4, 128, 100, act="f32", state_std=0.3, seed=9)
+    _announce(f"prefill decay fold paths act={act}")
+    x = synth.decode_inputs(1, 4, 128, 100, act=act, state_std=0.3, seed=9)
     x["alpha"][0, :, 0] = 1.7
     x["alpha"][0, :, 1] = -0.9
     x["alpha"][0, :, 2] = 1e-3
@@ -160,7 +165,7 @@ def test_decay_fold_paths():
     S, o = gpu_prefill(x, scale=0.25)
     S_ref, o_ref = oracle_decode(x, scale=0.25)
     check_state(f64(S), S_ref, torch.float32)
-    check_o(f64(o), o_ref, torch.float32)
+    check_o(f64(o), o_ref, DT[act])
 
 
 def test_offsets_beyond_2_31_elements():
@@ -220,3 +225,27 @@ def test_nan_stays_in_its_head():
     assert torch.isnan(o[1, :, 2]).any(dim=0).nonzero().flatten().tolist() == [17]
     assert not torch.isnan(o[2, :32, 4]).any()
     assert torch.isnan(o[2, 36, 4, 9])
+
+
+@pytest.mark.parametrize("tok", [5, 20])
+def test_nan_in_a_chunk_pair_stays_in_its_row(tok):
+    # bf16 activations (chunks taken in pairs): a NaN in one v entry (row 9) at token 5 (first
+    # chunk of the first pair) or 20 (second chunk) reaches row 9 of the state and of every
+    # later output of that head, and nothing else: the other rows, heads and sequences stay
+    # finite, and so do the outputs of the chunks before the NaN's own chunk.
+    _announce(f"prefill bf16 NaN at token {tok}")
+    x = synth.decode_inputs(2, 3, 128, 64, act="bf16", alpha_shift=-2.0, seed=13)
+    x["v"][1, tok, 2, 9] = float("nan")
+    S, o = gpu_prefill(x)
+    S, o = S.cpu().float(), o.cpu().float()
+    assert torch.isnan(S[1, 2]).any(dim=1).nonzero().flatten().tolist() == [9]
+    mask = torch.ones(2, 3, dtype=torch.bool)
+    mask[1, 2] = False
+    assert not torch.isnan(S[mask]).any() and not torch.isnan(o.permute(0, 2, 1, 3)[mask]).any()
+    head = o[1, :, 2]                                   # [T, D]
+    first = 16 * (tok // 16)                            # the NaN's chunk starts here
+    assert not torch.isnan(head[:first]).any()
+    assert torch.isnan(head[max(tok, first + 16):, 9]).all()
+    others = torch.ones(128, dtype=torch.bool)
+    others[9] = False
+    assert not torch.isnan(head[:, others]).any()
