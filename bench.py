@@ -180,8 +180,9 @@ def parse_args(argv=None):
     ap.add_argument("--probe-variant", type=int, default=-1,
                     help="probe_ workloads: geometry (-1 = that of the base workload's one-token "
                          "decode: 0 for a 4-byte state, 2 for a 2-byte state)")
-    ap.add_argument("--probe-group", type=int, default=1,
-                    help="probe_ workloads: consecutive tiles per XCD")
+    ap.add_argument("--probe-group", type=int, default=0,
+                    help="probe_ workloads: consecutive tiles per XCD (0 = the decode kernel's own "
+                         "order: 4 from 8192 heads and 16 below for a 4-byte state, 1 for 2-byte)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="write profiles/ summaries from the rocprofv3 CSVs under DIR")
     ap.add_argument("--profile-commands", action="store_true",
@@ -347,11 +348,12 @@ def time_gpu(args, workload: str, state_dtype: str, copy_ceiling: bool = False) 
     if kind == "probe":
         plib = _probe_lib()
         variant = args.probe_variant if args.probe_variant >= 0 else (0 if state_dtype == "f32" else 2)
+        group = args.probe_group or (1 if variant == 2 else (4 if heads >= 8192 else 16))
 
         def step(g):
             st = g["state"]
             rc = plib.gdn_stream_probe(ctypes.c_void_p(st.data_ptr()), st.numel() * st.element_size(),
-                                       heads, variant, args.probe_group,
+                                       heads, variant, group,
                                        ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
             if rc != 0:
                 raise RuntimeError(f"gdn_stream_probe failed ({rc})")

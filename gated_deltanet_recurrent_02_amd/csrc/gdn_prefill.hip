@@ -539,8 +539,9 @@ __device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
 // contracting over their 32 tokens on the 16 x 16 x 32 form:
 //     S'_end = S' + K0^T diag(Gam_end0 gamma1_15 / c_end) Delta0 + K1^T diag(Gam_end1 / c_end) Delta1,
 // c_end = gamma1_15 c_mid (folded into S' when out of [2^-64, 2^64], as in chunk_step). Same
-// algebra as two chunk_step calls; fp32 rounding differs. `prefetch` is called once the S'
-// products are done (it issues the next pair's loads into registers those products freed).
+// algebra as two chunk_step calls; fp32 rounding differs. `prefetch` issues the next pair's
+// loads before anything else (prompt workload 622 -> 593 us against issuing them after the S'
+// products: the longer the loads have, the fewer of the head's four waves miss in the L2).
 template <int D, int RT, typename AT, typename F>
 __device__ __forceinline__ void pair_step(f32x4 (&S)[RT][D / 16], float& c,
                                           const ChunkOps<D, RT, AT>& x0,
@@ -550,6 +551,8 @@ __device__ __forceinline__ void pair_step(f32x4 (&S)[RT][D / 16], float& c,
     static_assert(kBf16Mma<D, AT>, "the paired form runs on the bf16 matrix cores");
     constexpr int NMT = D / 16;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    prefetch();
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 X0[RT], Y0[RT], X1[RT], Y1[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) X0[r] = Y0[r] = X1[r] = Y1[r] = zero4;
@@ -590,10 +593,6 @@ __device__ __forceinline__ void pair_step(f32x4 (&S)[RT][D / 16], float& c,
         M = mfma_k32(ka0, ka1, M);
         N = mfma_k32(ka0, qa1, N);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    prefetch();
-    __builtin_amdgcn_sched_barrier(0);
-
     // First chunk, as in chunk_step.
     f32x4 Z0[RT], D0[RT], O0[RT];
     f32x4 gx0, gy0;
@@ -761,8 +760,7 @@ __global__ __launch_bounds__(64) void gdn_prefill_state_kernel(
     float cs = 1.0f;  // S = cs S' (wave-uniform)
     if constexpr (kBf16Mma<D, AT>) {
         // Chunks in pairs (pair_step); the next pair's operands load while the current pair
-        // computes, issued once its S' products have freed their registers. An odd last chunk
-        // runs alone.
+        // computes. An odd last chunk runs alone.
         ChunkOps<D, RT, AT> A0, A1, B0, B1;
         load_chunk<D, RT, AT>(A0, 0, T, H, b, h, row0, q, k, v, wsh, g, n);
         load_chunk<D, RT, AT>(A1, min(1, nch - 1), T, H, b, h, row0, q, k, v, wsh, g, n);
