@@ -243,20 +243,21 @@ def flops(spec: dict) -> int:
 PREFILL_CHUNK = 16
 
 
-def prefill_matrix_flops(spec: dict) -> dict:
-    """Matrix-core arithmetic one gdn_prefill call issues, per the chunked form's products
-    (chunks of 16 tokens, D = dk = dv, bf16 activations): per head and chunk
-      K S'^T, Q S'^T     2 x 16 x D x D x 2, each on three bf16 parts of S'   (bf16)
-      the state update   D x 16 x D x 2 on three bf16 parts of its factors      (bf16)
-      K Q^T              16 x 16 x D x 2                                        (bf16)
-      T Z, P Delta       2 x 16 x 16 x D x 2                                    (fp32)
-      prep: K K^T        16 x 16 x D x 2                                        (bf16)
+def prefill_matrix_flop(spec: dict) -> dict:
+    """Matrix-core arithmetic one gdn_prefill call issues (bf16 activations, chunks of 16
+    tokens taken in pairs, D = dk = dv), per head and chunk:
+      K S'^T on three bf16 parts of S', Q S'^T on two     (3 + 2) x 16 x D x D x 2   bf16
+      the state update on three bf16 parts of its factors 3 x D x 16 x D x 2         bf16
+      K Q^T, the prep's K K^T, and per pair K1 K0^T and Q1 K0^T (one per chunk)
+                                                          3 x 16 x 16 x D x 2        bf16
+      T Z, P Delta, and per pair the two corrections through Delta0 (one per chunk)
+                                                          3 x 16 x 16 x D x 2        fp32
     Returns bf16 and fp32 flop per call."""
     B, H, D, T = spec["B"], spec["H"], spec["D"], spec["T"]
     C = PREFILL_CHUNK
     chunks = B * H * math.ceil(T / C)
-    bf16 = chunks * (3 * 2 * C * D * D * 2 + 3 * D * C * D * 2 + C * C * D * 2 + C * C * D * 2)
-    f32 = chunks * (2 * C * C * D * 2)
+    bf16 = chunks * ((3 + 2) * C * D * D * 2 + 3 * D * C * D * 2 + 3 * C * C * D * 2)
+    f32 = chunks * (3 * C * C * D * 2)
     return {"bf16": bf16, "f32": f32}
 
 
@@ -503,7 +504,7 @@ def measure(args, workload: str, state_dtype: str, copy_ceiling: bool = False) -
         # form issues (three bf16 parts per fp32 operand) against the bf16 peak as well.
         sec = ms * 1e-3
         tf = flops(spec) / sec / 1e12
-        mf = prefill_matrix_flops(spec)
+        mf = prefill_matrix_flop(spec)
         issued_bf16 = mf["bf16"] / sec / 1e12
         r["roofline_hbm"] = r["roofline"]
         r["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_MFMA_TFLOPS,

@@ -22,9 +22,13 @@
 // per token; at D = 64 two waves share a head; below, one wave holds a whole head. Every wave
 // keeps its share of the window in registers for all T tokens of the call.
 // Only the slots the call wrote (one per token; all of them once T >= r) are stored back.
+// Multi-token calls on a bf16 window with bf16 activations at D = 128 run gdn_lowrank_mm_kernel
+// instead, which forms each round's key products on the matrix cores (see there).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "gdn_lowrank_launch.h"
 
@@ -417,6 +421,240 @@ void gdn_lowrank_kernel(LowrankArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ bf16 multi-token form
+
+typedef __bf16 lr_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float lr_f32x4 __attribute__((ext_vector_type(4)));
+
+// C += A B over a 16 x 16 x 32 slice, bf16 operands (lane l holds k = 8 (l/16) .. + 7 of its
+// row / column l % 16), fp32 accumulation into C[4 (l/16) + i][l % 16].
+__device__ __forceinline__ lr_f32x4 lr_mfma_k32(lr_u32x4 a, lr_u32x4 b, lr_f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(lr_bf16x8, a),
+                                                   __builtin_bit_cast(lr_bf16x8, b), c, 0, 0, 0);
+}
+
+// Multi-token calls on a bf16 window with bf16 activations at D = 128 (r = 16 or 32): the key
+// products of a whole round run on the matrix cores instead of per token on the vector ALUs.
+// Both operands are exact bf16 and the products accumulate in fp32, as in the vector form
+// (summation order differs). Per round of up to kLrRound tokens t0 .. t0+nt-1 (window slot p_r
+// the next to be written at the round's start):
+//   C[i][n]  = K_i . w_n   for every slot i,    C'[s][n] = k_{t0+s} . w_n,
+// with w_n = k_{t0+n} for n < 8 and q_{t0+n-8} for n >= 8, both on 16 x 16 x 32 bf16 products.
+// Token t0 + tn sees slot i's key as written at the round's start unless the round has already
+// rewritten it: slot i is written by round token s_i = (i - p_r) mod r, so for s_i < tn its key
+// is k_{t0+s_i} and its products are C'[s_i][.]. The merged products go to LDS once per round,
+// each wave computing them for every slot (the waves need every slot's totals for their write
+// columns), which removes the per-token key FMAs, slot sums and the per-token exchange and
+// barrier of the vector form. The per-token pass over the write columns is the vector form's.
+template <int R>
+__global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
+    constexpr int D = 128;
+    using AT = uint16_t;
+    using ST = uint16_t;
+    using G = LrGeo<D, R, AT, ST>;
+    static_assert(G::W == 2 && G::EU == 2 && G::SG == 2 && (R == 16 || R == 32), "layout");
+    constexpr int DW = G::DW, SG = G::SG, RS = G::RS, EU = G::EU, CL = G::CL;
+    constexpr int NTL = R / 16;     // 16-slot tiles of the key products
+    constexpr int TS = kLrRound;    // tokens per round
+    static_assert(TS == 8, "a round's k and q fill the 16 product columns");
+    __shared__ alignas(16) uint32_t kq_raw[2][TS][D / 2];   // the round's k and q (bf16 pairs)
+    __shared__ alignas(16) float vs[TS][D];                  // the round's v
+    __shared__ float tok_ab[2][TS];                          // [alpha, beta][token]
+    __shared__ alignas(16) float gram[2][TS][16];            // per wave: C'[s][n]
+    __shared__ alignas(16) float prod[2][2][TS][R];          // per wave: [K.k, K.q][token][slot]
+    __shared__ float kqd[2][TS];                             // per wave: k_t . q_t
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t head = blockIdx.x;
+    const int64_t b = head / a.H;
+    const int h = (int)(head - b * a.H);
+    const int gq = lane >> 4, mq = lane & 15;           // matrix-core lane coordinates
+    const int uc = w * DW + (lane % CL) * EU;           // first write column of this lane
+    const int sg = lane / CL;                           // slot group: slots [sg RS, (sg+1) RS)
+
+    ST* Uh = (ST*)a.U + head * (R * D);
+    ST* Kh = (ST*)a.K + head * (R * D);
+    float* ch = a.c + head * R;
+
+    // Keys in the matrix-core layout: lane (gq, mq) holds slot 16 t + mq, columns
+    // 8 gq + 32 s .. + 7 (s = 0..3), as raw bf16 pairs.
+    lr_u32x4 Km[NTL][4];
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            Km[t][s] = __builtin_nontemporal_load(
+                (const lr_u32x4*)(Kh + (16 * t + mq) * D + 8 * gq + 32 * s));
+    float Ur[RS][EU];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) load_run<ST, EU, kLrStateNT>(Uh + (sg * RS + i) * D + uc, Ur[i]);
+    float cl[RS];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) cl[i] = ch[sg * RS + i];
+    const uint32_t p0 = (uint32_t)a.pos[head] & (uint32_t)(R - 1);
+    uint32_t p = p0;
+    const int T = a.T;
+
+    for (int t0 = 0; t0 < T; t0 += TS) {
+        const int nt = min(TS, T - t0);
+        const uint32_t pr = p;   // slot of the round's first token
+        // Stage the round: k and q as raw bf16, v as floats (16-byte chunks, every load issued
+        // before any is waited for), and the gates.
+        constexpr int CPL = (TS * 3 * (D / 8) + 127) / 128;
+        lr_u32x4 raw[CPL];
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) {
+            const int c = tid + 128 * s;
+            if (c < nt * 3 * (D / 8)) {
+                const int j = c >> 4, col = (c & 15) * 8, which = j / nt, u = j - which * nt;
+                const AT* src = which == 0 ? (const AT*)a.k : which == 1 ? (const AT*)a.q
+                                                                        : (const AT*)a.v;
+                raw[s] = *(const lr_u32x4*)(src + ((b * T + t0 + u) * a.H + h) * D + col);
+            }
+        }
+        float gab = 0.0f;
+        if (tid < 2 * nt) {
+            const int u = tid % nt;
+            const int64_t gu = (b * T + t0 + u) * a.H + h;
+            gab = tid < nt ? a.alpha[gu] : a.beta[gu];
+        }
+        __syncthreads();         // the previous round's readers are done with the buffers
+#pragma unroll
+        for (int s = 0; s < CPL; ++s) {
+            const int c = tid + 128 * s;
+            if (c < nt * 3 * (D / 8)) {
+                const int j = c >> 4, col = (c & 15) * 8, which = j / nt, u = j - which * nt;
+                if (which < 2) {
+                    *(lr_u32x4*)&kq_raw[which][u][col / 2] = raw[s];
+                } else {
+                    const uint32_t wv[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vs[u][col + e] = Elt<AT>::get(wv[e >> 1], e & 1);
+                }
+            }
+        }
+        if (tid < 2 * nt) tok_ab[tid / nt][tid % nt] = gab;
+        __syncthreads();
+
+        // C (every slot) and C' (the round's keys) against the round's k | q columns.
+        lr_f32x4 C[NTL], Cp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) C[t] = lr_f32x4{0.f, 0.f, 0.f, 0.f};
+        const int vn = mq & 7;                 // the token of product column mq
+        const bool bval = vn < nt;
+        const bool aval = mq < nt;             // a row of C' that is a token of the round
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int wo = (8 * gq + 32 * s) / 2;
+            lr_u32x4 bv = *(const lr_u32x4*)&kq_raw[mq >> 3][vn][wo];
+            lr_u32x4 av = *(const lr_u32x4*)&kq_raw[0][vn][wo];
+            const lr_u32x4 z = {0u, 0u, 0u, 0u};
+            bv = bval ? bv : z;
+            av = aval ? av : z;
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) C[t] = lr_mfma_k32(Km[t][s], bv, C[t]);
+            Cp = lr_mfma_k32(av, bv, Cp);
+        }
+        // lane (gq, n = mq) holds C[t][e] = K_{16t + 4gq + e} . w_n and Cp[e] = k_{t0+4gq+e} . w_n
+        if (gq < 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gram[w][4 * gq + e][mq] = Cp[e];
+            if (mq >= 8 && ((mq - 8) >> 2) == gq) kqd[w][mq - 8] = Cp[(mq - 8) & 3];
+        }
+        __syncthreads();
+        // Merge: slot i rewritten by round token s_i < vn takes C'[s_i][n].
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            lr_f32x4 m;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t si = ((uint32_t)(16 * t + 4 * gq + e) - pr) & (uint32_t)(R - 1);
+                const float gv = gram[w][si < TS ? si : TS - 1][mq];
+                m[e] = si < (uint32_t)vn ? gv : C[t][e];
+            }
+            *(lr_f32x4*)&prod[w][mq >> 3][vn][16 * t + 4 * gq] = m;
+        }
+        __syncthreads();
+
+        for (int tt = 0; tt < nt; ++tt) {
+            const int64_t g = (b * T + t0 + tt) * a.H + h;
+            float vt[EU];
+#pragma unroll
+            for (int e = 0; e < EU; ++e) vt[e] = vs[tt][uc + e];
+            const float al = wave_uniform<true>(tok_ab[0][tt]);
+            const float be = wave_uniform<true>(tok_ab[1][tt]);
+            const float kq = wave_uniform<true>(kqd[w][tt]);
+            float u[EU], y[EU];
+#pragma unroll
+            for (int e = 0; e < EU; ++e) u[e] = y[e] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < RS; ++i) {
+                const int slot = sg * RS + i;
+                const float wu = cl[i] * prod[w][0][tt][slot];
+                const float wg = cl[i] * prod[w][1][tt][slot];
+                const float wy = (uint32_t)slot == p ? 0.0f : wg;
+#pragma unroll
+                for (int e = 0; e < EU; ++e) {
+                    u[e] = fmaf(wu, Ur[i][e], u[e]);
+                    y[e] = fmaf(wy, Ur[i][e], y[e]);
+                }
+            }
+            float d[EU], o[EU];
+#pragma unroll
+            for (int e = 0; e < EU; ++e) {
+                u[e] = column_sum<SG, CL>(u[e]);
+                y[e] = column_sum<SG, CL>(y[e]);
+                d[e] = be * fmaf(-al, u[e], vt[e]);
+                o[e] = a.scale * fmaf(al, y[e], kq * d[e]);
+            }
+            if (sg == 0) store_run<AT, EU>((AT*)a.o + g * D + uc, o);
+#pragma unroll
+            for (int i = 0; i < RS; ++i) {
+                const bool mine = (uint32_t)(sg * RS + i) == p;
+#pragma unroll
+                for (int e = 0; e < EU; ++e) Ur[i][e] = mine ? d[e] : Ur[i][e];
+                cl[i] = mine ? 1.0f : cl[i] * al;
+            }
+            p = (p + 1) & (uint32_t)(R - 1);
+        }
+        // The round's keys replace the slots it wrote (in registers, for the next round).
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            const uint32_t si = ((uint32_t)(16 * t + mq) - pr) & (uint32_t)(R - 1);
+            const bool mine = si < (uint32_t)nt;
+            const int sr = si < TS ? (int)si : TS - 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const lr_u32x4 kn = *(const lr_u32x4*)&kq_raw[0][sr][(8 * gq + 32 * s) / 2];
+                Km[t][s] = mine ? kn : Km[t][s];
+            }
+        }
+    }
+
+    // Store the slots this call wrote, every weight, and the next slot.
+    const uint32_t written = (uint32_t)(T < R ? T : R);
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+        if ((((uint32_t)(sg * RS + i) - p0) & (uint32_t)(R - 1)) < written)
+            store_run<ST, EU>(Uh + (sg * RS + i) * D + uc, Ur[i]);
+    if (w == 0) {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t)
+            if ((((uint32_t)(16 * t + mq) - p0) & (uint32_t)(R - 1)) < written) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    *(lr_u32x4*)(Kh + (16 * t + mq) * D + 8 * gq + 32 * s) = Km[t][s];
+            }
+        if (lane % CL == 0) {
+#pragma unroll
+            for (int i = 0; i < RS; ++i) ch[sg * RS + i] = cl[i];
+            if (lane == 0) a.pos[head] = (int32_t)p;
+        }
+    }
+}
+
 template <int D, int R, typename AT, typename ST>
 hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
     using G = LrGeo<D, R, AT, ST>;
@@ -427,6 +665,11 @@ hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
     void* argv[] = {&args};
     const void* fn = a.T == 1 ? (const void*)gdn_lowrank_kernel<D, R, AT, ST, true>
                               : (const void*)gdn_lowrank_kernel<D, R, AT, ST, false>;
+    if constexpr (D == 128 && (R == 16 || R == 32) && std::is_same<AT, uint16_t>::value &&
+                  std::is_same<ST, uint16_t>::value) {
+        // bf16 window and activations: several tokens take the matrix-core key products
+        if (a.T > 1) fn = (const void*)gdn_lowrank_mm_kernel<R>;
+    }
     return hipLaunchKernel(fn, dim3((uint32_t)heads), dim3(64 * G::W), argv, 0, stream);
 }
 

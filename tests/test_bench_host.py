@@ -57,16 +57,16 @@ def test_algorithmic_bytes_of_the_low_rank_workloads():
     assert bench.algorithmic_bytes(spec4, "bf16") == 256 * 48 * (read16 + write16 + 4 * token)
 
 
-def test_prefill_matrix_flops_of_the_prompt_workload():
-    # Per head and chunk of 16 tokens, D = 128: K S'^T and Q S'^T on three bf16 parts
-    # (3 x 2 x 16 x 128 x 128 x 2), the update on three parts (3 x 128 x 16 x 128 x 2), K Q^T and
-    # the prep's K K^T (2 x 16 x 16 x 128 x 2) in bf16; T Z and P Delta (2 x 16 x 16 x 128 x 2)
-    # in fp32. 4 x 48 heads x 256 chunks.
+def test_prefill_matrix_flop_of_the_prompt_workload():
+    # Per head and chunk of 16 tokens, D = 128: K S'^T on three bf16 parts of S' and Q S'^T on
+    # two ((3 + 2) x 16 x 128 x 128 x 2), the update on three parts (3 x 128 x 16 x 128 x 2),
+    # K Q^T, the prep's K K^T and the pair Grams (3 x 16 x 16 x 128 x 2) in bf16; T Z, P Delta
+    # and the pair corrections (3 x 16 x 16 x 128 x 2) in fp32. 4 x 48 heads x 256 chunks.
     spec = synth.WORKLOADS["prefill_b4_h48_d128_t4096"]
-    f = bench.prefill_matrix_flops(spec)
-    per_chunk_bf16 = 3 * 2 * 16 * 128 * 128 * 2 + 3 * 128 * 16 * 128 * 2 + 2 * 16 * 16 * 128 * 2
+    f = bench.prefill_matrix_flop(spec)
+    per_chunk_bf16 = 5 * 16 * 128 * 128 * 2 + 3 * 128 * 16 * 128 * 2 + 3 * 16 * 16 * 128 * 2
     assert f["bf16"] == 4 * 48 * 256 * per_chunk_bf16
-    assert f["f32"] == 4 * 48 * 256 * 2 * 16 * 16 * 128 * 2
+    assert f["f32"] == 4 * 48 * 256 * 3 * 16 * 16 * 128 * 2
     # the method's own arithmetic: 6 D^2 + 6 D per token and head
     assert bench.flops(spec) == 4 * 48 * 4096 * (6 * 128 * 128 + 6 * 128)
 
