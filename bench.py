@@ -88,6 +88,9 @@ EXTRA_CONFIGS = [
     ("lowrank_b256_r16_t1_f32", "lowrank_b256_h48_d128_r16_t1", "f32"),
     ("lowrank_b256_r16_t4_bf16", "lowrank_b256_h48_d128_r16_t4", "bf16"),
     ("stream_probe_b256_f32", "probe_decode_b256_h48_d128_t1", "f32"),
+    # the fastest in-place stream geometry of a sweep over 11 geometries x 5 XCD orders
+    # (4 rows per one-wave workgroup, runs of 2 tiles per XCD)
+    ("stream_probe_best_b256_f32", "probe_decode_b256_h48_d128_t1", "f32", {"probe_variant": 4, "probe_group": 2}),
 ]
 
 
@@ -153,7 +156,7 @@ ENTRY_POINTS = {"decode": "gdn_decode_step", "fused": "gdn_conv_gate_decode",
 KERNEL_NAMES = {"decode": ["gdn_decode_kernel"], "fused": ["gdn_conv_gate_decode_kernel"],
                 "verify": ["gdn_verify_kernel"],
                 "prefill": ["gdn_prefill_prep_kernel", "gdn_prefill_state_kernel"],
-                "lowrank": ["gdn_lowrank_kernel"], "probe": ["gdn_stream_probe_kernel"]}
+                "lowrank": ["gdn_lowrank_"], "probe": ["gdn_stream_probe_kernel"]}
 PROFILE_PREFIX = {"decode": "gdn_decode_kernel", "fused": "gdn_conv_gate_decode_kernel",
                   "verify": "gdn_verify_kernel", "prefill": "gdn_prefill",
                   "lowrank": "gdn_lowrank_kernel", "probe": "gdn_stream_probe_kernel"}
@@ -689,6 +692,11 @@ def summarize(root: str, workload: str, state_dtype: str, out_dir: str = PROFILE
     missing = [k for k in names if k not in trace]
     if missing:
         raise ValueError(f"{tp}: no row for {missing}")
+    import re
+    disp = {}
+    for k in names:
+        m = re.search(r"(gdn_\w+?)(<|\()", trace[k]["Name"])
+        disp[k] = m.group(1) if m else k
     lines += ["Kernels: " + "; ".join(f"`{trace[k]['Name']}`" for k in names), "",
               "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
               f"Command: `{cmds['trace']}`", "",
@@ -697,7 +705,7 @@ def summarize(root: str, workload: str, state_dtype: str, out_dir: str = PROFILE
     for k in names:
         r = trace[k]
         avg_ns += float(r["AverageNs"])
-        lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+        lines.append(f"| {disp[k]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
                      f"{r['MaxNs']} | {float(r['StdDev']):.0f} |")
     lines.append("")
     per_launch_gbps = alg / (avg_ns * 1e-9) / 1e9
@@ -749,7 +757,7 @@ def summarize(root: str, workload: str, state_dtype: str, out_dir: str = PROFILE
             wk += w_
             by = f_ * 1024 * fscale + w_ * 1024 * wscale
             hbm += by
-            lines.append(f"| {k} | {f_:.1f} ({fe[k]['n']['FETCH_SIZE']}) | {w_:.1f} "
+            lines.append(f"| {disp[k]} | {f_:.1f} ({fe[k]['n']['FETCH_SIZE']}) | {w_:.1f} "
                          f"({wr[k]['n']['WRITE_SIZE']}) | {by:.0f} |")
         lines += ["", f"Measured HBM bytes per launch {hbm:.0f} vs algorithmic {alg} "
                       f"({100 * (hbm / alg - 1):+.1f}%).", ""]
@@ -773,7 +781,7 @@ def summarize(root: str, workload: str, state_dtype: str, out_dir: str = PROFILE
             rb = 32 * r32 + 64 * r64 + 128 * r128
             wb = 64 * w64 + 32 * (wtot - w64)
             req_bytes += rb + wb
-            lines.append(f"| {k} | {r32:.0f} / {r64:.0f} / {r128:.0f} | {rtot:.0f} | {w64:.0f} of "
+            lines.append(f"| {disp[k]} | {r32:.0f} / {r64:.0f} / {r128:.0f} | {rtot:.0f} | {w64:.0f} of "
                          f"{wtot:.0f} | {rb:.0f} | {wb:.0f} |")
         lines += ["", f"By request size: {req_bytes:.0f} bytes per launch vs algorithmic {alg} "
                       f"({100 * (req_bytes / alg - 1):+.1f}%).", ""]
@@ -796,7 +804,7 @@ def summarize(root: str, workload: str, state_dtype: str, out_dir: str = PROFILE
             v = vb.get(k, {}).get("mean", {})
             res = sq[k]["res"]
             lines.append(
-                f"| {k} | {waves:.0f} | {m['SQ_INSTS_VALU'] / waves:.1f} | {m['SQ_INSTS_MFMA'] / waves:.1f} | "
+                f"| {disp[k]} | {waves:.0f} | {m['SQ_INSTS_VALU'] / waves:.1f} | {m['SQ_INSTS_MFMA'] / waves:.1f} | "
                 f"{100 * m['SQ_ACTIVE_INST_VALU'] / (256 * cyc):.1f} | "
                 f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * cyc):.1f} | "
                 f"{m['SQ_WAIT_INST_ANY'] / max(1.0, m['SQ_WAVE_CYCLES']):.2f} | "
@@ -895,9 +903,12 @@ def main(argv=None):
     line["frac_of_copy_bw"] = r["gbps"] / r["copy_gbps_same_bytes"]
     if headline and not args.no_extra:
         configs = {}
-        for label, wl, sdt in EXTRA_CONFIGS:
+        for label, wl, sdt, *over in EXTRA_CONFIGS:
             try:
-                configs[label] = _config_entry(measure(args, wl, sdt))
+                a2 = argparse.Namespace(**{**vars(args), **(over[0] if over else {})})
+                configs[label] = _config_entry(measure(a2, wl, sdt))
+                if over:
+                    configs[label].update(over[0])
             except Exception as e:  # a failing extra config must not hide the headline line
                 configs[label] = {"workload": wl, "state_dtype": sdt, "error": repr(e)[:300]}
             print(f"[bench] {label}: {json.dumps(configs[label])[:200]}", file=sys.stderr, flush=True)
@@ -905,6 +916,9 @@ def main(argv=None):
         probe = configs.get("stream_probe_b256_f32", {})
         if "us" in probe:
             line["frac_of_same_pattern_probe"] = probe["us"] / r["us"]
+        best = configs.get("stream_probe_best_b256_f32", {})
+        if "us" in best:
+            line["frac_of_best_stream_probe"] = best["us"] / r["us"]
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         if kind == "probe":
