@@ -988,20 +988,26 @@ constexpr int64_t kOneTokenSpreadHeads = 8192;
 //    B = 160 and 192 tie;
 //  * one token, bf16 state: all rows of a head in one workgroup, 8 rows per wave, 8 lanes per
 //    row (two 16-byte loads per lane and row): 140 -> 130 us at B=256 H=48 D=128 against 16
-//    lanes per row (fp32 states show no difference);
+//    lanes per row (fp32 states show no difference); runs of 4 heads per XCD: 128.2 -> 124.9
+//    us (2: 126.5 us); the multi-token 16-bit calls take the same order (decode T = 4 156.4 ->
+//    154.4 us, verify 184.4 -> 183.4, fused unchanged);
 //  * several tokens (and the fused path): the per-token arithmetic is repeated on registers,
 //    so occupancy and instruction count decide: 16 rows per wave, one workgroup per head,
 //    8 lanes per row where it saves reduction steps (bf16 state, fused prologue);
-//  * several tokens, fp32 state, decode: one wave per workgroup again (16 rows, the 8 tiles
-//    of a head kept on one XCD so its q and k come from one L2): 2% faster than a workgroup
-//    per head at B=256 H=48 D=128 T=4, where the verify kernel is 3% slower with it; 8 rows
-//    per wave (16 tiles per head) is slower (277 -> 302 us);
+//  * several tokens, fp32 state, decode: one wave per workgroup again (16 rows): 2% faster
+//    than a workgroup per head at B=256 H=48 D=128 T=4, where the verify kernel is 3% slower
+//    with it; 8 rows per wave (16 tiles per head) is slower (277 -> 302 us); runs of 2 tiles
+//    per XCD: 273.4 -> 266.2 us against a head's 8 tiles on one XCD (runs of 1 and 4: 277.8,
+//    275.0 us);
+//  * verify, fp32 state: a workgroup per head, runs of 2 heads per XCD (272.0 -> 267.8 us
+//    against 1; 4: 269.0 us);
 //  * fused path, fp32 state: 4 waves of 32 rows per head (190 VGPRs, two workgroups per CU):
 //    2.5% faster than 8 waves of 16 rows at B=256 H=48 D=128 T=4; 16-bit states lose 9% with
-//    it. The fused kernel needs the whole head in one workgroup (the conv state of the q and
-//    k channels is read and rewritten by it).
+//    it; runs of 4 heads per XCD: 277.6 -> 263.8 us against 1 (2: 267.8 us). The fused kernel
+//    needs the whole head in one workgroup (the conv state of the q and k channels is read and
+//    rewritten by it).
 template <int D, typename ST> struct DecodeOneToken {  // 2-byte states
-    using G = Geo<D, ST, D / 8, 1, 1, true, true, 1, 8>;
+    using G = Geo<D, ST, D / 8, 1, 1, true, true, 4, 8>;
 };
 template <int D> struct DecodeOneToken<D, float> {
     using G = Geo<D, float, 1, D / 8, 1, true, true, 4>;
@@ -1009,24 +1015,24 @@ template <int D> struct DecodeOneToken<D, float> {
 };
 
 template <int D, typename ST> struct DecodeTokens {  // 2-byte states
-    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 1, 8>;
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 4, 8>;
 };
 template <int D> struct DecodeTokens<D, float> {
-    using G = Geo<D, float, 1, max_int(1, D / 16), 8, true, true, max_int(1, D / 16), 16>;
+    using G = Geo<D, float, 1, max_int(1, D / 16), 8, true, true, 2, 16>;
 };
 
 template <int D, typename ST> struct VerifyTokens {  // 2-byte states
-    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 1, 8>;
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 4, 8>;
 };
 template <int D> struct VerifyTokens<D, float> {
-    using G = Geo<D, float, max_int(1, D / 16), 1, 8, true, true, 1, 16>;
+    using G = Geo<D, float, max_int(1, D / 16), 1, 8, true, true, 2, 16>;
 };
 
 template <int D, typename ST> struct FusedTokens {  // 2-byte states
-    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 1, 8>;
+    using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 4, 8>;
 };
 template <int D> struct FusedTokens<D, float> {
-    using G = Geo<D, float, max_int(1, D / 32), 1, 8, true, true, 1, 8>;
+    using G = Geo<D, float, max_int(1, D / 32), 1, 8, true, true, 4, 8>;
 };
 
 template <int D, typename ST, typename AT>
