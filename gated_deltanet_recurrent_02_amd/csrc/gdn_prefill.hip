@@ -90,14 +90,25 @@ __device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
 // product with a bf16 operand is then an fp32-exact product split over three bf16 products
 // (an fp32 value carries 24 significant bits). Non-finite values stay non-finite.
 struct Split3 { uint32_t h, m, l; };
+
+// The high halves of two words packed into one, x's in the low half: (x >> 16) | (y & 0xffff0000)
+// in one byte permute (v_perm_b32 picks bytes 2, 3 of x and 2, 3 of y).
+__device__ __forceinline__ uint32_t hi_halves(uint32_t x, uint32_t y) {
+    return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+// The low halves likewise: (x & 0xffff) | (y << 16).
+__device__ __forceinline__ uint32_t lo_halves(uint32_t x, uint32_t y) {
+    return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+
 __device__ __forceinline__ Split3 split3(float a, float b) {
     constexpr uint32_t HI = 0xffff0000u;
     const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
     const float ra = a - __uint_as_float(ua & HI), rb = b - __uint_as_float(ub & HI);
     const uint32_t va = __float_as_uint(ra), vb = __float_as_uint(rb);
     const float sa = ra - __uint_as_float(va & HI), sb = rb - __uint_as_float(vb & HI);
-    return Split3{(ua >> 16) | (ub & HI), (va >> 16) | (vb & HI),
-                  (__float_as_uint(sa) >> 16) | (__float_as_uint(sb) & HI)};
+    return Split3{hi_halves(ua, ub), hi_halves(va, vb),
+                  hi_halves(__float_as_uint(sa), __float_as_uint(sb))};
 }
 
 // bf16 activations of head dim >= 32 take the bf16 matrix-core path (k and q are exact bf16
@@ -498,8 +509,8 @@ __device__ __forceinline__ void chunk_step(f32x4 (&S)[RT][D / 16], float& c,
         for (int mt = 0; mt < NMT; ++mt) {
             const int wi = mt >> 1;
             const uint32_t k0 = x.ku[0].w[wi], k1 = x.ku[1].w[wi], k2 = x.ku[2].w[wi], k3 = x.ku[3].w[wi];
-            const u32x2 ka = (mt & 1) ? u32x2{(k0 >> 16) | (k1 & 0xffff0000u), (k2 >> 16) | (k3 & 0xffff0000u)}
-                                      : u32x2{(k0 & 0xffffu) | (k1 << 16), (k2 & 0xffffu) | (k3 << 16)};
+            const u32x2 ka = (mt & 1) ? u32x2{hi_halves(k0, k1), hi_halves(k2, k3)}
+                                      : u32x2{lo_halves(k0, k1), lo_halves(k2, k3)};
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 S[r][mt] = mfma_k16(ka, dh[r], S[r][mt]);
@@ -696,10 +707,8 @@ __device__ __forceinline__ void pair_step(f32x4 (&S)[RT][D / 16], float& c,
         const uint32_t a0 = x0.ku[0].w[wi], a1 = x0.ku[1].w[wi], a2 = x0.ku[2].w[wi], a3 = x0.ku[3].w[wi];
         const uint32_t b0 = x1.ku[0].w[wi], b1 = x1.ku[1].w[wi], b2 = x1.ku[2].w[wi], b3 = x1.ku[3].w[wi];
         const u32x4 ka = (mt & 1)
-            ? u32x4{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u),
-                    (b0 >> 16) | (b1 & 0xffff0000u), (b2 >> 16) | (b3 & 0xffff0000u)}
-            : u32x4{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16),
-                    (b0 & 0xffffu) | (b1 << 16), (b2 & 0xffffu) | (b3 << 16)};
+            ? u32x4{hi_halves(a0, a1), hi_halves(a2, a3), hi_halves(b0, b1), hi_halves(b2, b3)}
+            : u32x4{lo_halves(a0, a1), lo_halves(a2, a3), lo_halves(b0, b1), lo_halves(b2, b3)};
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             S[r][mt] = mfma_k32(ka, dh[r], S[r][mt]);
