@@ -1,14 +1,18 @@
 """Property tests on the GPU: random shapes, dtypes, token counts and seeds, drawn by
 hypothesis (derandomized, so every run draws the same cases), each compared with the fp64
-oracle at the parity bars. Covers gdn_decode_step and gdn_lowrank_decode_step."""
+oracle at the parity bars. Covers gdn_decode_step, gdn_lowrank_decode_step, gdn_prefill,
+gdn_conv_gate_decode and gdn_decode_verify (two rounds and a commit)."""
+import numpy as np
 import pytest
 import torch
 from hypothesis import HealthCheck, given, settings
 from hypothesis import strategies as st
 
+import gated_deltanet_recurrent_02_amd as gdn
+import oracle
 from gated_deltanet_recurrent_02_amd import synth
 from parity import (check_lowrank, check_o, check_state, f64, gpu_decode, gpu_lowrank,
-                    oracle_decode, oracle_lowrank)
+                    oracle_decode, oracle_lowrank, oracle_prefix_all, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,3 +47,81 @@ def test_lowrank_random_cases(B, H, T, D, r, act, sdt, window, seed):
     x = synth.lowrank_inputs(B, H, D, T, r, act=act, state_dtype=sdt, window=window, seed=seed)
     g, o = gpu_lowrank(x)
     check_lowrank(g, o, oracle_lowrank(x), DT[act], DT[sdt])
+
+
+@SETTINGS
+@given(B=st.integers(1, 3), H=st.integers(1, 4), T=st.integers(1, 90),
+       D=st.sampled_from([16, 32, 64, 128]), act=st.sampled_from(["f32", "bf16", "f16"]),
+       sdt=st.sampled_from(["f32", "bf16", "f16"]), shift=st.sampled_from([2.0, -2.0]),
+       scale=st.sampled_from([1.0, 0.5]), seed=st.integers(0, 2 ** 16))
+def test_prefill_random_cases(B, H, T, D, act, sdt, shift, scale, seed):
+    print(f"[case] prefill B={B} H={H} T={T} D={D} act={act} state={sdt} seed={seed}", flush=True)
+    x = synth.decode_inputs(B, H, D, T, act=act, state_dtype=sdt, alpha_shift=shift,
+                            state_std=0.3, seed=seed)
+    g = to_dev(x)
+    o = gdn.prefill(g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["state"], scale=scale)
+    torch.cuda.synchronize()
+    S_ref, o_ref = oracle_decode(x, scale=scale)
+    check_state(f64(g["state"]), S_ref, DT[sdt])
+    check_o(f64(o), o_ref, DT[act])
+
+
+@SETTINGS
+@given(B=st.integers(1, 4), H=st.integers(1, 5), T=st.integers(1, 12),
+       D=st.sampled_from([16, 32, 64, 128]), sdt=st.sampled_from(["f32", "bf16", "f16"]),
+       bias=st.booleans(), seed=st.integers(0, 2 ** 16))
+def test_fused_random_cases(B, H, T, D, sdt, bias, seed):
+    print(f"[case] fused B={B} H={H} T={T} D={D} state={sdt} bias={bias} seed={seed}", flush=True)
+    x = synth.fused_inputs(B, H, D, T, state_dtype=sdt, with_bias=bias, seed=seed)
+    g = to_dev(x)
+    o = gdn.conv_gate_decode(g["qkv"], g["conv_state"], g["conv_w"], g["conv_b"], g["a_logit"],
+                             g["b_logit"], g["state"])
+    torch.cuda.synchronize()
+    cb = None if x["conv_b"] is None else f64(x["conv_b"])
+    S_ref, o_ref, cs_ref = oracle.gdn_conv_gate_decode(
+        f64(x["qkv"]), f64(x["conv_state"]), f64(x["conv_w"]), cb, f64(x["a_logit"]),
+        f64(x["b_logit"]), f64(x["state"]), H=H, dk=D, dv=D)
+    assert np.array_equal(f64(g["conv_state"]), cs_ref)
+    check_state(f64(g["state"]), S_ref, DT[sdt])
+    check_o(f64(o), o_ref, torch.bfloat16)
+
+
+@SETTINGS
+@given(B=st.integers(1, 5), H=st.integers(1, 4), T1=st.integers(1, 10), T2=st.integers(1, 10),
+       D=st.sampled_from([16, 32, 64, 128]), sdt=st.sampled_from(["f32", "bf16", "f16"]),
+       data=st.data(), seed=st.integers(0, 2 ** 16))
+def test_verify_random_rounds(B, H, T1, T2, D, sdt, data, seed):
+    # Round 1 drafts T1 tokens from the start state; round 2 commits an accepted prefix of
+    # round 1 and drafts T2 tokens; a commit-only call commits a prefix of round 2. Prefix
+    # lengths are drawn per sequence, including 0 and the full round (and out of range, which
+    # the kernel clamps).
+    n1 = data.draw(st.lists(st.integers(-1, T1 + 1), min_size=B, max_size=B))
+    n2 = data.draw(st.lists(st.integers(-1, T2 + 1), min_size=B, max_size=B))
+    print(f"[case] verify B={B} H={H} T={T1}/{T2} D={D} state={sdt} n1={n1} n2={n2} seed={seed}",
+          flush=True)
+    x1 = synth.decode_inputs(B, H, D, T1, state_dtype=sdt, alpha_shift=-1.0, state_std=0.3,
+                             seed=seed)
+    x2 = synth.decode_inputs(B, H, D, T2, state_dtype=sdt, alpha_shift=-1.0, state_std=0.3,
+                             seed=seed + 1)
+    tok = ("q", "k", "v", "alpha", "beta")
+    g1, g2 = to_dev(x1), to_dev(x2)
+    state = g1["state"]
+    o1, d1 = gdn.decode_verify(*(g1[n] for n in tok), state)
+    o2, d2 = gdn.decode_verify(*(g2[n] for n in tok), state,
+                               prev=(torch.tensor(n1, dtype=torch.int32).cuda(), g1["k"],
+                                     g1["alpha"], d1))
+    torch.cuda.synchronize()
+    S_c1 = f64(state)
+    empty = tuple(g2[n][:, :0].contiguous() for n in tok)
+    gdn.decode_verify(*empty, state, prev=(torch.tensor(n2, dtype=torch.int32).cuda(), g2["k"],
+                                           g2["alpha"], d2))
+    torch.cuda.synchronize()
+    _, o1_ref = oracle_decode(x1)
+    check_o(f64(o1), o1_ref, torch.bfloat16)
+    S1c = oracle_prefix_all(x1, n1)
+    check_state(S_c1, S1c, DT[sdt], what="committed state after round 1's prefix")
+    x2s = dict(x2, state=torch.from_numpy(S1c))
+    _, o2_ref = oracle_decode(x2s)
+    check_o(f64(o2), o2_ref, torch.bfloat16)
+    check_state(f64(state), oracle_prefix_all(x2s, n2), DT[sdt],
+                what="committed state after round 2's prefix")
