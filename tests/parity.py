@@ -5,7 +5,12 @@ then the maximum over heads, so that a head with small values cannot hide behind
 Bars (floating point):
   * fp32 state after all tokens: 1e-4; bf16-stored state: 2e-2 (its own rounding is 2^-8);
     fp16-stored state: 1e-3 (one rounding of 2^-11 relative, twice that for margin);
-  * fp32 o: 1e-4;
+  * fp32 o: 1e-4 per token, relative to max(max|R_t|, 1e-3 max|R_head|): a token whose output
+    is a small cancelling sum (alpha_t = 0 with k_t . q_t near 0, say) is held to 1e-7 of its
+    head's largest output in absolute terms, since fp32 evaluation of a D-term dot product
+    carries an absolute error of order sqrt(D) 2^-24 times its terms (the token-by-token kernel
+    and the chunked form both show 6e-10 on such a token whose output is 8.5e-7 of a head at
+    0.44);
   * bf16 o: 2e-2 per head, and elementwise |o - R| <= 2^-8 |R| + 1e-4 max|R_head| (one rounding
     to bf16 of an fp32 value that is itself within ~1e-6 of R); fp16 o: 1e-3 per head and
     elementwise |o - R| <= 2^-11 |R| + 1e-4 max|R_head|.
@@ -49,16 +54,24 @@ def check_state(state_gpu: np.ndarray, ref: np.ndarray, dtype: torch.dtype, what
 
 def check_o(o_gpu: np.ndarray, ref: np.ndarray, dtype: torch.dtype, heads_axis_last: bool = True):
     """o arrays [..., H, dv] (heads on the second-last axis)."""
-    e = head_rel_err(o_gpu, ref, 1)
     if dtype == torch.float32:
-        assert e <= TOL_O_F32, f"o: per-head relative error {e:.3e} > {TOL_O_F32}"
-    else:
-        tol, ulp = (TOL_O_BF16, 2.0 ** -8) if dtype == torch.bfloat16 else (1e-3, 2.0 ** -11)
-        assert e <= tol, f"o: per-head relative error {e:.3e} > {tol}"
-        scale = np.abs(ref).max(axis=-1, keepdims=True)
-        bound = ulp * np.abs(ref) + 1e-4 * scale
-        bad = np.abs(o_gpu - ref) > bound
-        assert not bad.any(), f"o: {int(bad.sum())} elements beyond one rounding to {dtype}"
+        d = np.abs(o_gpu - ref).max(axis=-1)
+        n = np.abs(ref).max(axis=-1)
+        # The head's largest output: over the tokens (axis 1) of [B, T, H] maxima, else overall.
+        head = n.max(axis=1, keepdims=True) if n.ndim == 3 else np.full_like(n, n.max())
+        if np.any(np.isnan(d)):
+            e = float("inf")
+        else:
+            e = float(np.max(d / np.maximum(np.maximum(n, 1e-3 * head), 1e-300)))
+        assert e <= TOL_O_F32, f"o: per-token relative error {e:.3e} > {TOL_O_F32}"
+        return e
+    e = head_rel_err(o_gpu, ref, 1)
+    tol, ulp = (TOL_O_BF16, 2.0 ** -8) if dtype == torch.bfloat16 else (1e-3, 2.0 ** -11)
+    assert e <= tol, f"o: per-head relative error {e:.3e} > {tol}"
+    scale = np.abs(ref).max(axis=-1, keepdims=True)
+    bound = ulp * np.abs(ref) + 1e-4 * scale
+    bad = np.abs(o_gpu - ref) > bound
+    assert not bad.any(), f"o: {int(bad.sum())} elements beyond one rounding to {dtype}"
     return e
 
 
