@@ -87,6 +87,7 @@ EXTRA_CONFIGS = [
     ("prefill_b4_t4096_f32", "prefill_b4_h48_d128_t4096", "f32"),
     ("lowrank_b256_r16_t1_f32", "lowrank_b256_h48_d128_r16_t1", "f32"),
     ("lowrank_b256_r16_t4_bf16", "lowrank_b256_h48_d128_r16_t4", "bf16"),
+    ("lowrank_b256_r32_t8_bf16", "lowrank_b256_h48_d128_r32_t8", "bf16"),
     ("stream_probe_b256_f32", "probe_decode_b256_h48_d128_t1", "f32"),
     # the fastest in-place stream geometry of a sweep over 11 geometries x 5 XCD orders
     # (4 rows per one-wave workgroup, runs of 2 tiles per XCD)

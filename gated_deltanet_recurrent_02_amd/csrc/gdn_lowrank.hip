@@ -22,8 +22,10 @@
 // per token; at D = 64 two waves share a head; below, one wave holds a whole head. Every wave
 // keeps its share of the window in registers for all T tokens of the call.
 // Only the slots the call wrote (one per token; all of them once T >= r) are stored back.
-// Multi-token calls on a bf16 window with bf16 activations at D = 128 run gdn_lowrank_mm_kernel
-// instead, which forms each round's key products on the matrix cores (see there).
+// Multi-token calls on a bf16 window with bf16 activations at D = 128 run
+// gdn_lowrank_mm_kernel instead, which forms each round's key products on the matrix cores, or
+// from a few tokens on (kLrRoundFormTokens) gdn_lowrank_round_kernel, which takes each round
+// of tokens in matrix form on the matrix cores (see there).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -178,6 +180,13 @@ constexpr int lr_max_waves() { return sizeof(ST) == 4 && R >= 32 ? 4 : 2; }
 constexpr bool kLrStateNT = true;
 // Tokens per staged round of a multi-token call.
 constexpr int kLrRound = 8;
+// Multi-token calls on a bf16 window (D = 128, bf16 activations) from this many tokens on run
+// each round in matrix form (gdn_lowrank_round_kernel), shorter ones one token at a time over
+// the write columns (gdn_lowrank_mm_kernel). Crossovers measured on MI355X at B = 256, H = 48:
+// 16 slots: T = 4 48.0 vs 55.0 us, T = 6 57.1 vs 57.6, T = 7 61.9 vs 58.5, T = 16 116.1 vs
+// 99.1; 32 slots: T = 3 84.0 vs 83.9, T = 4 91.2 vs 85.0, T = 16 224.1 vs 145.2.
+template <int R>
+constexpr int kLrRoundFormTokens = R >= 32 ? 4 : 7;
 
 // Geometry of one instance: head dim D, window R, storage types AT (activations), ST (state).
 template <int D, int R, typename AT, typename ST>
@@ -432,6 +441,11 @@ __device__ __forceinline__ lr_f32x4 lr_mfma_k32(lr_u32x4 a, lr_u32x4 b, lr_f32x4
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(lr_bf16x8, a),
                                                    __builtin_bit_cast(lr_bf16x8, b), c, 0, 0, 0);
 }
+// C += A B over a 16 x 16 x 4 slice in fp32: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; same accumulator layout.
+__device__ __forceinline__ lr_f32x4 lr_mfma4(float a, float b, lr_f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 // Multi-token calls on a bf16 window with bf16 activations at D = 128 (r = 16 or 32): the key
 // products of a whole round run on the matrix cores instead of per token on the vector ALUs.
@@ -655,6 +669,312 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
     }
 }
 
+// Multi-token calls on a bf16 window with bf16 activations at D = 128 (r = 16 or 32) run each
+// round of up to kLrRound tokens in matrix form on the matrix cores. Round tokens n = 0..nt-1
+// (window slot p_r the next to be written at the round's start) write slots p_r + n, so slot i
+// is rewritten by round token s_i = (i - p_r) mod r if s_i < nt. With A_n = alpha_0 ...
+// alpha_{n-1} (the decay of the window's old slots at token n) and G_ns = alpha_{s+1} ...
+// alpha_{n-1} (that of the round's own write s), the window before token n is the old slots
+// with s_i >= n, weights c_i A_n, plus the round's writes s < n, weights G_ns, so
+//     u_n = X_n + sum_{s<n} G_ns (k_s . k_n) delta_s,   X_n = sum_{s_i >= n} c_i A_n (K_i . k_n) U_i
+// and delta_n = beta_n (v_n - alpha_n u_n) gives, over the round,
+//     Delta = T Z,  T = (I + L)^-1,  Z = diag(beta) V - diag(alpha beta) X,
+//     L_ns = beta_n alpha_n G_ns (k_s . k_n) (s < n, strictly lower triangular).
+// The readout (the slot token n evicts drops out of y_n; the others decay, delta_n joins) is
+//     O = scale (diag(alpha) Y + diag(k . q) Delta) = Y' + M Z,   M = L' T,
+//     Y'_n = scale alpha_n sum_{s_i > n} c_i A_n (K_i . q_n) U_i,
+//     L'_ns = scale alpha_n G_ns (k_s . q_n) (s < n),  L'_nn = scale (k_n . q_n).
+// Per round: the key products K_i . [k | q] and the round's Gram (bf16 16 x 16 x 32, as exact
+// bf16 operands into fp32), then on fp32 16 x 16 x 4 products over the lane's write columns
+// one product of the [X; Y'] weights (16 x r, the key products times c_i, the decays and the
+// masks) with the window's writes (r x 128), and one of [T; M] (16 x 8, formed by forward
+// substitution on eight lanes) with Z. Rows 0..7 of the results are Delta, rows 8..15 the
+// outputs; the rewritten slots take their rows of Delta. Both waves of a head form every
+// product over their own 64 write columns.
+template <int R>
+__global__ __launch_bounds__(128) void gdn_lowrank_round_kernel(LowrankArgs a) {
+    constexpr int D = 128;
+    using AT = uint16_t;
+    using ST = uint16_t;
+    static_assert(R == 16 || R == 32, "16- or 32-slot windows");
+    constexpr int NTL = R / 16;     // 16-slot tiles of the key products
+    constexpr int NS = R / 4;       // window slots per lane in the write products
+    constexpr int TS = kLrRound;    // tokens per round
+    static_assert(TS == 8, "a round's k and q fill the 16 product columns");
+    constexpr int VST = D + 4;      // row stride of the staged v (rows 4 apart in other banks)
+    constexpr int KST = D / 2 + 4;  // row stride (words) of staged keys: rows in other banks
+    __shared__ alignas(16) uint32_t ks[R][KST];              // the window's keys (bf16 pairs)
+    __shared__ alignas(16) uint32_t kq_raw[2][TS][KST];      // the round's k and q (bf16 pairs)
+    __shared__ alignas(16) float vs[TS][VST];                // the round's v
+    __shared__ float tok_ab[2][TS];                          // [alpha, beta][token]
+    __shared__ float dec[2][TS + 1];                         // prefix / suffix decay products
+    __shared__ float gram[2][16][TS + 1];                    // per wave: [k | q]_n . k_s at [n][s]
+    __shared__ float lmat[2][2][TS][TS];                     // per wave: L, L'
+    __shared__ alignas(16) float tm[2][16][TS];              // per wave: [T; M]
+    // Per wave: Delta on its columns. It shares the staged k and q's storage: every read of
+    // those in a round (key products, key replacement) is behind the barrier that precedes the
+    // first write of Delta, and the next round stages after its own barrier.
+    static_assert(sizeof(float) * 2 * TS * 64 <= sizeof(kq_raw), "Delta fits the staging");
+    float (*dl)[TS][64] = reinterpret_cast<float (*)[TS][64]>(&kq_raw[0][0][0]);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t head = blockIdx.x;
+    const int64_t b = head / a.H;
+    const int h = (int)(head - b * a.H);
+    const int gq = lane >> 4, mq = lane & 15;           // matrix-core lane coordinates
+    const int col0 = 64 * w + 4 * mq;                    // this lane's four write columns
+
+    ST* Uh = (ST*)a.U + head * (R * D);
+    ST* Kh = (ST*)a.K + head * (R * D);
+    float* ch = a.c + head * R;
+
+    // Staging: thread tid moves token su = tid / 16, columns 8 (tid % 16) .. + 7 of k, q and v;
+    // tokens past the round are staged as zeros with alpha = beta = 0, which makes their rows
+    // and columns of every product below exactly zero. A round's loads are issued one round
+    // ahead (the first with the window's), so they land while the previous round computes.
+    const int su = tid >> 4, scol = (tid & 15) * 8;
+    const int64_t tok_stride = (int64_t)a.H * D;
+    const int T = a.T;
+    lr_u32x4 rk, rq, rv;
+    float gab;
+    auto stage_loads = [&](int t0) {
+        const int nt = min(TS, T - t0);
+        rk = rq = rv = lr_u32x4{0u, 0u, 0u, 0u};
+        if (su < nt) {
+            const int64_t off = ((b * T + t0) * a.H + h) * D + su * tok_stride + scol;
+            rk = *(const lr_u32x4*)((const AT*)a.k + off);
+            rq = *(const lr_u32x4*)((const AT*)a.q + off);
+            rv = *(const lr_u32x4*)((const AT*)a.v + off);
+        }
+        gab = 0.0f;
+        if (tid < 2 * TS && (tid & 7) < nt) {
+            const int64_t gu = (b * T + t0 + (tid & 7)) * a.H + h;
+            gab = tid < TS ? a.alpha[gu] : a.beta[gu];
+        }
+    };
+    stage_loads(0);
+
+    // The window's keys in LDS, one copy per head (thread tid moves 16-byte chunks
+    // tid + 128 j: slot chunk / 16, columns 8 (chunk % 16) .. + 7).
+    lr_u32x4 kc[R / 8];
+#pragma unroll
+    for (int j = 0; j < R / 8; ++j) {
+        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
+        kc[j] = __builtin_nontemporal_load((const lr_u32x4*)(Kh + row * D + cw8));
+    }
+    // Writes and weights: lane (gq, mq) holds slot slot_of(s) = 16 (s / 4) + 4 gq + s % 4 (the
+    // slot whose key products it holds as C[s / 4][s % 4]), columns col0 .. col0 + 3.
+    auto slot_of = [&](int s) { return 16 * (s >> 2) + 4 * gq + (s & 3); };
+    float Uw[NS][4], cw[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        load_run<ST, 4, kLrStateNT>(Uh + slot_of(s) * D + col0, Uw[s]);
+        cw[s] = ch[slot_of(s)];
+    }
+    const uint32_t p0 = (uint32_t)a.pos[head] & (uint32_t)(R - 1);
+    uint32_t p = p0;
+#pragma unroll
+    for (int j = 0; j < R / 8; ++j) {
+        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
+        *(lr_u32x4*)&ks[row][cw8 / 2] = kc[j];
+    }
+
+    for (int t0 = 0; t0 < T; t0 += TS) {
+        const int nt = min(TS, T - t0);
+        const uint32_t pr = p;   // slot of the round's first token
+        __syncthreads();         // the previous round's readers are done with the buffers
+        *(lr_u32x4*)&kq_raw[0][su][scol / 2] = rk;   // (the first round's barrier also covers ks)
+        *(lr_u32x4*)&kq_raw[1][su][scol / 2] = rq;
+        {
+            const uint32_t wv[4] = {rv.x, rv.y, rv.z, rv.w};
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = Elt<AT>::get(wv[e >> 1], e & 1);
+            *(lr_f32x4*)&vs[su][scol] = lr_f32x4{f[0], f[1], f[2], f[3]};
+            *(lr_f32x4*)&vs[su][scol + 4] = lr_f32x4{f[4], f[5], f[6], f[7]};
+        }
+        if (tid < 2 * TS) tok_ab[tid >> 3][tid & 7] = gab;
+        if (t0 + TS < T) stage_loads(t0 + TS);
+        __syncthreads();
+        // Decays: dec[0][j] = alpha_0 ... alpha_{j-1} (A_j), dec[1][j] = alpha_j ... alpha_{nt-1}.
+        if (tid < 2 * (TS + 1)) {
+            const int j = tid % (TS + 1);
+            const bool suffix = tid > TS;
+            float pd = 1.0f;
+#pragma unroll
+            for (int m = 0; m < TS; ++m) {
+                const bool in = suffix ? (m >= j && m < nt) : m < j;
+                pd = in ? pd * tok_ab[0][m] : pd;
+            }
+            dec[suffix ? 1 : 0][j] = pd;
+        }
+
+        // Key products: C[t][e] = K_{16t + 4gq + e} . w_mq for every slot, and the round's Gram
+        // Cp[e] = k_{4gq + e} . w_mq, with w_n = k_n for n < 8 and q_{n-8} for n >= 8.
+        lr_f32x4 C[NTL], Cp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) C[t] = lr_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int wo = (8 * gq + 32 * s) / 2;
+            const lr_u32x4 bv = *(const lr_u32x4*)&kq_raw[mq >> 3][mq & 7][wo];
+            const lr_u32x4 av = *(const lr_u32x4*)&kq_raw[0][mq & 7][wo];   // rows >= 8 unused
+#pragma unroll
+            for (int t = 0; t < NTL; ++t)
+                C[t] = lr_mfma_k32(*(const lr_u32x4*)&ks[16 * t + mq][wo], bv, C[t]);
+            Cp = lr_mfma_k32(av, bv, Cp);
+        }
+        if (gq < 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gram[w][mq][4 * gq + e] = Cp[e];
+        }
+        __syncthreads();
+
+        // Row factors of this lane's product row mq: token m = mq % 8 of X (mq < 8) or Y'
+        // (mq >= 8); X rows take the old slots with s_i >= m, Y' rows those with s_i > m.
+        const int tokr = mq & 7;
+        const float am = dec[0][tokr], alr = tok_ab[0][tokr], ber = tok_ab[1][tokr];
+        const float rf = mq < 8 ? alr * ber * am : a.scale * alr * am;
+        const uint32_t thr = mq < 8 ? (uint32_t)mq : (uint32_t)(mq - 7);
+        // [alpha beta X; Y'] over the window's old slots: 16 x r weights times r x 128 writes
+        // (issued before the solve below, which runs on the vector ALUs meanwhile).
+        lr_f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = lr_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint32_t si = ((uint32_t)slot_of(s) - pr) & (uint32_t)(R - 1);
+            const float wgt = si >= thr ? rf * cw[s] * C[s >> 2][s & 3] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] = lr_mfma4(wgt, Uw[s][t], acc[t]);
+        }
+
+        // Every key product of the round is formed: the round's keys replace the slots it
+        // writes (read again by the next round's products, after its barriers).
+        if (su < nt)
+            *(lr_u32x4*)&ks[(pr + (uint32_t)su) & (uint32_t)(R - 1)][scol / 2] =
+                *(const lr_u32x4*)&kq_raw[0][su][scol / 2];
+
+        // L and L': lane (n, s) = (lane / 8, lane % 8), decays as running products (never
+        // ratios). Tokens past the round have zero gates and keys, so their entries are zero.
+        {
+            const int nn = lane >> 3, ss = lane & 7;
+            float gm = 1.0f;
+#pragma unroll
+            for (int m = 1; m < TS - 1; ++m) gm = (m > ss && m < nn) ? gm * tok_ab[0][m] : gm;
+            const float an = tok_ab[0][nn], bn = tok_ab[1][nn];
+            const float gkk = gram[w][nn][ss], gkq = gram[w][8 + nn][ss];
+            lmat[w][0][nn][ss] = ss < nn ? bn * an * gm * gkk : 0.0f;
+            lmat[w][1][nn][ss] = ss < nn ? a.scale * an * gm * gkq : ss == nn ? a.scale * gkq : 0.0f;
+        }
+        __syncthreads();
+        // T = (I + L)^-1 by forward substitution and M = L' T, column c = lane % 8 (lanes 0..7
+        // store it).
+        {
+            const int cc = lane & 7;
+            float x[TS];
+#pragma unroll
+            for (int nn = 0; nn < TS; ++nn) {
+                float acc1 = nn == cc ? 1.0f : 0.0f;
+#pragma unroll
+                for (int ss = 0; ss < nn; ++ss) acc1 = fmaf(-lmat[w][0][nn][ss], x[ss], acc1);
+                x[nn] = acc1;
+            }
+            if (lane < TS) {
+#pragma unroll
+                for (int nn = 0; nn < TS; ++nn) {
+                    float acc1 = 0.0f;
+#pragma unroll
+                    for (int ss = 0; ss <= nn; ++ss) acc1 = fmaf(lmat[w][1][nn][ss], x[ss], acc1);
+                    tm[w][nn][cc] = x[nn];
+                    tm[w][TS + nn][cc] = acc1;
+                }
+            }
+        }
+        __syncthreads();   // [T; M] is in LDS
+
+        // Per tile: Z = diag(beta) V - alpha beta X on rows 0..7 (lanes gq < 2, rows 4 gq + i),
+        // zero elsewhere; the accumulator keeps Y' on rows 8..15 and restarts rows 0..7 at zero;
+        // then [Delta; O] += [T; M] Z with the contraction index 4 gq + s in step s (each lane's
+        // own Z rows are its b operand).
+        {
+            const lr_f32x4 tv = *(const lr_f32x4*)&tm[w][mq][4 * (gq & 1)];
+            const int r0 = 4 * (gq & 1);
+            float av[4], bz[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = gq < 2 ? tv[i] : 0.0f;
+                bz[i] = tok_ab[1][r0 + i];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float z[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    z[i] = gq < 2 ? fmaf(bz[i], vs[r0 + i][col0 + t], -acc[t][i]) : 0.0f;
+                acc[t] = gq < 2 ? lr_f32x4{0.f, 0.f, 0.f, 0.f} : acc[t];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[t] = lr_mfma4(av[s], z[s], acc[t]);
+            }
+        }
+        if (gq >= 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * (gq - 2) + i;
+                if (m < nt) {
+                    const float ov[4] = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+                    store_run<AT, 4>((AT*)a.o + ((b * T + t0 + m) * a.H + h) * D + col0, ov);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *(lr_f32x4*)&dl[w][4 * gq + i][4 * mq] =
+                    lr_f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+        }
+        __syncthreads();
+        // The slots the round wrote take their rows of Delta and weight alpha_{s+1} ...
+        // alpha_{nt-1}; the others decay by A_nt.
+        const float anl = dec[0][nt];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint32_t si = ((uint32_t)slot_of(s) - pr) & (uint32_t)(R - 1);
+            if (si < (uint32_t)nt) {
+                const lr_f32x4 d = *(const lr_f32x4*)&dl[w][si][4 * mq];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) Uw[s][t] = d[t];
+                cw[s] = dec[1][si + 1];
+            } else {
+                cw[s] *= anl;
+            }
+        }
+        p = (pr + (uint32_t)nt) & (uint32_t)(R - 1);
+    }
+
+    // Store the slots this call wrote, every weight, and the next slot.
+    const uint32_t written = (uint32_t)(T < R ? T : R);
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if ((((uint32_t)slot_of(s) - p0) & (uint32_t)(R - 1)) < written)
+            store_run<ST, 4>(Uh + slot_of(s) * D + col0, Uw[s]);
+    __syncthreads();   // the last round's keys are in ks
+#pragma unroll
+    for (int j = 0; j < R / 8; ++j) {
+        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
+        if ((((uint32_t)row - p0) & (uint32_t)(R - 1)) < written)
+            *(lr_u32x4*)(Kh + row * D + cw8) = *(const lr_u32x4*)&ks[row][cw8 / 2];
+    }
+    if (w == 0) {
+        if (mq == 0) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) ch[slot_of(s)] = cw[s];
+            if (lane == 0) a.pos[head] = (int32_t)p;
+        }
+    }
+}
+
 template <int D, int R, typename AT, typename ST>
 hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
     using G = LrGeo<D, R, AT, ST>;
@@ -667,8 +987,10 @@ hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
                               : (const void*)gdn_lowrank_kernel<D, R, AT, ST, false>;
     if constexpr (D == 128 && (R == 16 || R == 32) && std::is_same<AT, uint16_t>::value &&
                   std::is_same<ST, uint16_t>::value) {
-        // bf16 window and activations: several tokens take the matrix-core key products
-        if (a.T > 1) fn = (const void*)gdn_lowrank_mm_kernel<R>;
+        // bf16 window and activations: several tokens take the matrix-core key products; from
+        // kLrRoundFormTokens<R> tokens on, each round runs in matrix form
+        if (a.T >= kLrRoundFormTokens<R>) fn = (const void*)gdn_lowrank_round_kernel<R>;
+        else if (a.T > 1) fn = (const void*)gdn_lowrank_mm_kernel<R>;
     }
     return hipLaunchKernel(fn, dim3((uint32_t)heads), dim3(64 * G::W), argv, 0, stream);
 }

@@ -51,6 +51,7 @@ WORKLOADS = {
     "lowrank_b256_h48_d128_r16_t1": dict(B=256, H=48, D=128, T=1, act="bf16", r=16, lowrank=True),
     "lowrank_b256_h48_d128_r32_t1": dict(B=256, H=48, D=128, T=1, act="bf16", r=32, lowrank=True),
     "lowrank_b256_h48_d128_r16_t4": dict(B=256, H=48, D=128, T=4, act="bf16", r=16, lowrank=True),
+    "lowrank_b256_h48_d128_r32_t8": dict(B=256, H=48, D=128, T=8, act="bf16", r=32, lowrank=True),
     # speculative verify rounds of 4 tokens; the accepted prefix per sequence is drawn by
     # accepted_prefix() below
     "verify_b256_h48_d128_t4": dict(B=256, H=48, D=128, T=4, act="bf16", state_init="normal",

@@ -107,7 +107,7 @@ def test_verify_workload_rounds_all_heads(sdt):
 
 
 @pytest.mark.parametrize("name", ["lowrank_b256_h48_d128_r16_t1", "lowrank_b256_h48_d128_r32_t1",
-                                  "lowrank_b256_h48_d128_r16_t4"])
+                                  "lowrank_b256_h48_d128_r16_t4", "lowrank_b256_h48_d128_r32_t8"])
 @pytest.mark.parametrize("sdt", ["f32", "bf16"])
 def test_lowrank_workloads_all_heads(name, sdt):
     _announce(f"{name} state={sdt} (all 12288 heads)")
