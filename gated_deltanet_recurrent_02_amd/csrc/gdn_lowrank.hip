@@ -24,8 +24,8 @@
 // Only the slots the call wrote (one per token; all of them once T >= r) are stored back.
 // Multi-token calls on a bf16 window with bf16 activations at D = 128 run
 // gdn_lowrank_mm_kernel instead, which forms each round's key products on the matrix cores, or
-// from a few tokens on (kLrRoundFormTokens) gdn_lowrank_round_kernel, which takes each round
-// of tokens in matrix form on the matrix cores (see there).
+// (when its rounds are full or nearly so, lr_round_form) gdn_lowrank_round_kernel, which takes
+// each round of tokens in matrix form on the matrix cores (see there).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -180,13 +180,16 @@ constexpr int lr_max_waves() { return sizeof(ST) == 4 && R >= 32 ? 4 : 2; }
 constexpr bool kLrStateNT = true;
 // Tokens per staged round of a multi-token call.
 constexpr int kLrRound = 8;
-// Multi-token calls on a bf16 window (D = 128, bf16 activations) from this many tokens on run
-// each round in matrix form (gdn_lowrank_round_kernel), shorter ones one token at a time over
-// the write columns (gdn_lowrank_mm_kernel). Crossovers measured on MI355X at B = 256, H = 48:
-// 16 slots: T = 4 48.0 vs 55.0 us, T = 6 57.1 vs 57.6, T = 7 61.9 vs 58.5, T = 16 116.1 vs
-// 99.1; 32 slots: T = 3 84.0 vs 83.9, T = 4 91.2 vs 85.0, T = 16 224.1 vs 145.2.
-template <int R>
-constexpr int kLrRoundFormTokens = R >= 32 ? 4 : 7;
+// Multi-token calls on a bf16 window (D = 128, bf16 activations) run each round in matrix form
+// (gdn_lowrank_round_kernel) when every round is full or nearly so (a partial last round costs
+// what a full one does), else one token at a time over the write columns
+// (gdn_lowrank_mm_kernel). Measured on MI355X at B = 256, H = 48 (per-token / round form, us):
+// 16 slots T = 4 42.3 / 54.9, T = 8 64.3 / 60.6, T = 10 82.6 / 92.6, T = 12 92.0 / 95.1,
+// T = 16 113.0 / 99.7, T = 24 150.4 / 132.7; 32 slots T = 4 65.2 / 84.8, T = 6 83.7 / 87.3,
+// T = 8 96.6 / 88.2, T = 10 124.6 / 140.7, T = 16 171.5 / 145.5, T = 24 241.7 / 201.2.
+__host__ __device__ constexpr bool lr_round_form(int T) {
+    return T >= kLrRound && (T % kLrRound == 0 || T % kLrRound >= kLrRound - 2);
+}
 
 // Geometry of one instance: head dim D, window R, storage types AT (activations), ST (state).
 template <int D, int R, typename AT, typename ST>
@@ -471,7 +474,9 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
     constexpr int NTL = R / 16;     // 16-slot tiles of the key products
     constexpr int TS = kLrRound;    // tokens per round
     static_assert(TS == 8, "a round's k and q fill the 16 product columns");
-    __shared__ alignas(16) uint32_t kq_raw[2][TS][D / 2];   // the round's k and q (bf16 pairs)
+    constexpr int KST = D / 2 + 4;  // row stride (words) of staged keys: rows in other banks
+    __shared__ alignas(16) uint32_t ks[R][KST];              // the window's keys (bf16 pairs)
+    __shared__ alignas(16) uint32_t kq_raw[2][TS][KST];      // the round's k and q (bf16 pairs)
     __shared__ alignas(16) float vs[TS][D];                  // the round's v
     __shared__ float tok_ab[2][TS];                          // [alpha, beta][token]
     __shared__ alignas(16) float gram[2][TS][16];            // per wave: C'[s][n]
@@ -492,15 +497,37 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
     ST* Kh = (ST*)a.K + head * (R * D);
     float* ch = a.c + head * R;
 
-    // Keys in the matrix-core layout: lane (gq, mq) holds slot 16 t + mq, columns
-    // 8 gq + 32 s .. + 7 (s = 0..3), as raw bf16 pairs.
-    lr_u32x4 Km[NTL][4];
+    // Staging: thread tid moves token su = tid / 16, columns 8 (tid % 16) .. + 7 of k, q and v;
+    // tokens past the round are staged as zeros (their products are never read).
+    const int su = tid >> 4, scol = (tid & 15) * 8;
+    const int64_t tok_stride = (int64_t)a.H * D;
+    const int T = a.T;
+    lr_u32x4 rk, rq, rv;
+    float gab;
+    auto stage_loads = [&](int t0) {
+        const int nt = min(TS, T - t0);
+        rk = rq = rv = lr_u32x4{0u, 0u, 0u, 0u};
+        if (su < nt) {
+            const int64_t off = ((b * T + t0) * a.H + h) * D + su * tok_stride + scol;
+            rk = *(const lr_u32x4*)((const AT*)a.k + off);
+            rq = *(const lr_u32x4*)((const AT*)a.q + off);
+            rv = *(const lr_u32x4*)((const AT*)a.v + off);
+        }
+        gab = 0.0f;
+        if (tid < 2 * TS && (tid & 7) < nt) {
+            const int64_t gu = (b * T + t0 + (tid & 7)) * a.H + h;
+            gab = tid < TS ? a.alpha[gu] : a.beta[gu];
+        }
+    };
+    stage_loads(0);
+    // The window's keys in LDS, one copy per head (thread tid moves 16-byte chunks
+    // tid + 128 j: slot chunk / 16, columns 8 (chunk % 16) .. + 7).
+    lr_u32x4 kc[R / 8];
 #pragma unroll
-    for (int t = 0; t < NTL; ++t)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            Km[t][s] = __builtin_nontemporal_load(
-                (const lr_u32x4*)(Kh + (16 * t + mq) * D + 8 * gq + 32 * s));
+    for (int j = 0; j < R / 8; ++j) {
+        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
+        kc[j] = __builtin_nontemporal_load((const lr_u32x4*)(Kh + row * D + cw8));
+    }
     float Ur[RS][EU];
 #pragma unroll
     for (int i = 0; i < RS; ++i) load_run<ST, EU, kLrStateNT>(Uh + (sg * RS + i) * D + uc, Ur[i]);
@@ -509,47 +536,28 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
     for (int i = 0; i < RS; ++i) cl[i] = ch[sg * RS + i];
     const uint32_t p0 = (uint32_t)a.pos[head] & (uint32_t)(R - 1);
     uint32_t p = p0;
-    const int T = a.T;
+#pragma unroll
+    for (int j = 0; j < R / 8; ++j) {
+        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
+        *(lr_u32x4*)&ks[row][cw8 / 2] = kc[j];
+    }
 
     for (int t0 = 0; t0 < T; t0 += TS) {
         const int nt = min(TS, T - t0);
         const uint32_t pr = p;   // slot of the round's first token
-        // Stage the round: k and q as raw bf16, v as floats (16-byte chunks, every load issued
-        // before any is waited for), and the gates.
-        constexpr int CPL = (TS * 3 * (D / 8) + 127) / 128;
-        lr_u32x4 raw[CPL];
-#pragma unroll
-        for (int s = 0; s < CPL; ++s) {
-            const int c = tid + 128 * s;
-            if (c < nt * 3 * (D / 8)) {
-                const int j = c >> 4, col = (c & 15) * 8, which = j / nt, u = j - which * nt;
-                const AT* src = which == 0 ? (const AT*)a.k : which == 1 ? (const AT*)a.q
-                                                                        : (const AT*)a.v;
-                raw[s] = *(const lr_u32x4*)(src + ((b * T + t0 + u) * a.H + h) * D + col);
-            }
-        }
-        float gab = 0.0f;
-        if (tid < 2 * nt) {
-            const int u = tid % nt;
-            const int64_t gu = (b * T + t0 + u) * a.H + h;
-            gab = tid < nt ? a.alpha[gu] : a.beta[gu];
-        }
         __syncthreads();         // the previous round's readers are done with the buffers
+        *(lr_u32x4*)&kq_raw[0][su][scol / 2] = rk;   // (the first round's barrier also covers ks)
+        *(lr_u32x4*)&kq_raw[1][su][scol / 2] = rq;
+        {
+            const uint32_t wv[4] = {rv.x, rv.y, rv.z, rv.w};
+            float f[8];
 #pragma unroll
-        for (int s = 0; s < CPL; ++s) {
-            const int c = tid + 128 * s;
-            if (c < nt * 3 * (D / 8)) {
-                const int j = c >> 4, col = (c & 15) * 8, which = j / nt, u = j - which * nt;
-                if (which < 2) {
-                    *(lr_u32x4*)&kq_raw[which][u][col / 2] = raw[s];
-                } else {
-                    const uint32_t wv[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) vs[u][col + e] = Elt<AT>::get(wv[e >> 1], e & 1);
-                }
-            }
+            for (int e = 0; e < 8; ++e) f[e] = Elt<AT>::get(wv[e >> 1], e & 1);
+            *(lr_f32x4*)&vs[su][scol] = lr_f32x4{f[0], f[1], f[2], f[3]};
+            *(lr_f32x4*)&vs[su][scol + 4] = lr_f32x4{f[4], f[5], f[6], f[7]};
         }
-        if (tid < 2 * nt) tok_ab[tid / nt][tid % nt] = gab;
+        if (tid < 2 * TS) tok_ab[tid >> 3][tid & 7] = gab;
+        if (t0 + TS < T) stage_loads(t0 + TS);
         __syncthreads();
 
         // C (every slot) and C' (the round's keys) against the round's k | q columns.
@@ -557,18 +565,14 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
 #pragma unroll
         for (int t = 0; t < NTL; ++t) C[t] = lr_f32x4{0.f, 0.f, 0.f, 0.f};
         const int vn = mq & 7;                 // the token of product column mq
-        const bool bval = vn < nt;
-        const bool aval = mq < nt;             // a row of C' that is a token of the round
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int wo = (8 * gq + 32 * s) / 2;
-            lr_u32x4 bv = *(const lr_u32x4*)&kq_raw[mq >> 3][vn][wo];
-            lr_u32x4 av = *(const lr_u32x4*)&kq_raw[0][vn][wo];
-            const lr_u32x4 z = {0u, 0u, 0u, 0u};
-            bv = bval ? bv : z;
-            av = aval ? av : z;
+            const lr_u32x4 bv = *(const lr_u32x4*)&kq_raw[mq >> 3][vn][wo];
+            const lr_u32x4 av = *(const lr_u32x4*)&kq_raw[0][vn][wo];   // rows >= 8 unused
 #pragma unroll
-            for (int t = 0; t < NTL; ++t) C[t] = lr_mfma_k32(Km[t][s], bv, C[t]);
+            for (int t = 0; t < NTL; ++t)
+                C[t] = lr_mfma_k32(*(const lr_u32x4*)&ks[16 * t + mq][wo], bv, C[t]);
             Cp = lr_mfma_k32(av, bv, Cp);
         }
         // lane (gq, n = mq) holds C[t][e] = K_{16t + 4gq + e} . w_n and Cp[e] = k_{t0+4gq+e} . w_n
@@ -633,18 +637,11 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
             }
             p = (p + 1) & (uint32_t)(R - 1);
         }
-        // The round's keys replace the slots it wrote (in registers, for the next round).
-#pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-            const uint32_t si = ((uint32_t)(16 * t + mq) - pr) & (uint32_t)(R - 1);
-            const bool mine = si < (uint32_t)nt;
-            const int sr = si < TS ? (int)si : TS - 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const lr_u32x4 kn = *(const lr_u32x4*)&kq_raw[0][sr][(8 * gq + 32 * s) / 2];
-                Km[t][s] = mine ? kn : Km[t][s];
-            }
-        }
+        // The round's keys replace the slots it wrote (every key product of the round was
+        // formed before the barrier that precedes the per-token pass).
+        if (su < nt)
+            *(lr_u32x4*)&ks[(pr + (uint32_t)su) & (uint32_t)(R - 1)][scol / 2] =
+                *(const lr_u32x4*)&kq_raw[0][su][scol / 2];
     }
 
     // Store the slots this call wrote, every weight, and the next slot.
@@ -653,14 +650,14 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
     for (int i = 0; i < RS; ++i)
         if ((((uint32_t)(sg * RS + i) - p0) & (uint32_t)(R - 1)) < written)
             store_run<ST, EU>(Uh + (sg * RS + i) * D + uc, Ur[i]);
+    __syncthreads();   // the last round's keys are in ks
+#pragma unroll
+    for (int j = 0; j < R / 8; ++j) {
+        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
+        if ((((uint32_t)row - p0) & (uint32_t)(R - 1)) < written)
+            *(lr_u32x4*)(Kh + row * D + cw8) = *(const lr_u32x4*)&ks[row][cw8 / 2];
+    }
     if (w == 0) {
-#pragma unroll
-        for (int t = 0; t < NTL; ++t)
-            if ((((uint32_t)(16 * t + mq) - p0) & (uint32_t)(R - 1)) < written) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    *(lr_u32x4*)(Kh + (16 * t + mq) * D + 8 * gq + 32 * s) = Km[t][s];
-            }
         if (lane % CL == 0) {
 #pragma unroll
             for (int i = 0; i < RS; ++i) ch[sg * RS + i] = cl[i];
@@ -987,9 +984,9 @@ hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
                               : (const void*)gdn_lowrank_kernel<D, R, AT, ST, false>;
     if constexpr (D == 128 && (R == 16 || R == 32) && std::is_same<AT, uint16_t>::value &&
                   std::is_same<ST, uint16_t>::value) {
-        // bf16 window and activations: several tokens take the matrix-core key products; from
-        // kLrRoundFormTokens<R> tokens on, each round runs in matrix form
-        if (a.T >= kLrRoundFormTokens<R>) fn = (const void*)gdn_lowrank_round_kernel<R>;
+        // bf16 window and activations: several tokens take the matrix-core key products, and
+        // rounds that are full or nearly so run in matrix form
+        if (lr_round_form(a.T)) fn = (const void*)gdn_lowrank_round_kernel<R>;
         else if (a.T > 1) fn = (const void*)gdn_lowrank_mm_kernel<R>;
     }
     return hipLaunchKernel(fn, dim3((uint32_t)heads), dim3(64 * G::W), argv, 0, stream);

@@ -244,13 +244,13 @@ def test_zero_decay_keeps_only_the_new_write():
 
 
 # Multi-token calls on a bf16 window with bf16 activations at D = 128 take each round of up to
-# 8 tokens in matrix form (the round's writes through a triangular solve) from 7 tokens on with
-# 16 slots and from 4 on with 32 (shorter calls take the per-token form); the cases below reach
-# both sides of that switch, partial rounds, several rounds, wraps of the window within and
-# across rounds, and the gate extremes.
+# 8 tokens in matrix form (the round's writes through a triangular solve) when every round is
+# full or nearly so (T >= 8 with T % 8 in {0, 6, 7}), else the per-token form; the cases below
+# reach both forms, partial rounds, several rounds, wraps of the window within and across
+# rounds, and the gate extremes.
 
 @pytest.mark.parametrize("r", [16, 32])
-@pytest.mark.parametrize("T", [2, 3, 4, 6, 7, 8, 9, 13, 53])
+@pytest.mark.parametrize("T", [2, 3, 4, 6, 7, 8, 9, 13, 14, 15, 16, 22, 53])
 def test_rounds_on_bf16_windows(r, T):
     _announce(f"lowrank rounds B=2 H=3 D=128 r={r} T={T} act=bf16 state=bf16")
     x = synth.lowrank_inputs(2, 3, 128, T, r, act="bf16", state_dtype="bf16", alpha_shift=-1.0,
@@ -259,12 +259,13 @@ def test_rounds_on_bf16_windows(r, T):
     check_lowrank(g, o, oracle_lowrank(x, scale=0.6), torch.bfloat16, torch.bfloat16)
 
 
+@pytest.mark.parametrize("T", [11, 14])
 @pytest.mark.parametrize("window", ["filled", "empty"])
-def test_rounds_gate_extremes(window):
+def test_rounds_gate_extremes(window, T):
     # Per head: alpha = 1 with beta = 0 (writes exactly zero, weights kept), alpha = 0 (earlier
     # writes drop out), alpha = 0 on every third token only, beta = 1, and negative alpha.
-    _announce(f"lowrank rounds gate extremes window={window}")
-    x = synth.lowrank_inputs(2, 5, 128, 11, 16, act="bf16", state_dtype="bf16", window=window,
+    _announce(f"lowrank rounds gate extremes window={window} T={T}")
+    x = synth.lowrank_inputs(2, 5, 128, T, 16, act="bf16", state_dtype="bf16", window=window,
                              seed=31)
     x["alpha"][:, :, 0] = 1.0
     x["beta"][:, :, 0] = 0.0
@@ -277,20 +278,21 @@ def test_rounds_gate_extremes(window):
     # alpha = 1, beta = 0: every write is zero and the untouched slots keep their weights.
     for b in range(2):
         p = int(x["pos"][b, 0]) & 15
-        written = [(p + t) % 16 for t in range(11)]
+        written = [(p + t) % 16 for t in range(T)]
         assert bool((g["U"][b, 0, written] == 0).all())
         kept = [i for i in range(16) if i not in written]
         assert torch.equal(g["c"][b, 0, kept].cpu(), x["c"][b, 0, kept])
         assert bool((g["c"][b, 0, written] == 1.0).all())
 
 
-def test_rounds_nan_stays_in_its_head():
+@pytest.mark.parametrize("T", [12, 14])
+def test_rounds_nan_stays_in_its_head(T):
     # A NaN in one head's v at token 9 (the second round) poisons only that head, and there
     # only from its own round on: the products of the round form multiply it by the structural
     # zeros of T and M (0 * NaN = NaN), so the earlier tokens of its round are not asserted,
     # while the first round's outputs stay finite.
-    _announce("lowrank rounds NaN isolation")
-    x = synth.lowrank_inputs(2, 4, 128, 12, 16, act="bf16", state_dtype="bf16", seed=32)
+    _announce(f"lowrank rounds NaN isolation T={T}")
+    x = synth.lowrank_inputs(2, 4, 128, T, 16, act="bf16", state_dtype="bf16", seed=32)
     x["v"][1, 9, 3, 7] = float("nan")
     g, o = gpu_lowrank(x)
     for b in range(2):
@@ -305,14 +307,14 @@ def test_rounds_nan_stays_in_its_head():
 
 
 def test_rounds_split_calls_continue_the_window():
-    # 19 tokens as calls of 5, 1 and 13 tokens (round boundaries differ from one call's). The
+    # 22 tokens as calls of 5, 1 and 16 tokens (round boundaries differ from one call's). The
     # window is stored in bf16 between calls, so the oracle runs call by call from the window
     # the previous call stored (U rounded to bf16; K is a copy of bf16 keys; c and pos exact).
     _announce("lowrank rounds split calls")
-    x = synth.lowrank_inputs(2, 5, 128, 19, 16, act="bf16", state_dtype="bf16", seed=33)
+    x = synth.lowrank_inputs(2, 5, 128, 22, 16, act="bf16", state_dtype="bf16", seed=33)
     g = to_dev(x)
     win = {n: x[n] for n in LOWRANK_STATE}
-    for a, z in ((0, 5), (5, 6), (6, 19)):
+    for a, z in ((0, 5), (5, 6), (6, 22)):
         part = {n: x[n][:, a:z].contiguous() for n in ("q", "k", "v", "alpha", "beta")}
         o = gdn.lowrank_decode_step(*(g[n][:, a:z].contiguous()
                                       for n in ("q", "k", "v", "alpha", "beta")),
@@ -324,10 +326,10 @@ def test_rounds_split_calls_continue_the_window():
 
 
 def test_rounds_graph_replays_match_eager():
-    # Three 9-token calls captured in one HIP graph, replayed three times with eager work
+    # Three 16-token calls captured in one HIP graph, replayed three times with eager work
     # between the replays; every replay must equal the eager calls on a copy of the state.
     _announce("lowrank rounds graph replay")
-    x = synth.lowrank_inputs(4, 48, 128, 9, 16, act="bf16", state_dtype="bf16", seed=34)
+    x = synth.lowrank_inputs(4, 48, 128, 16, 16, act="bf16", state_dtype="bf16", seed=34)
     g = to_dev(x)
     e = to_dev(x)
     stream = torch.cuda.Stream()
