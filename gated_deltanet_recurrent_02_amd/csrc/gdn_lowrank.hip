@@ -438,6 +438,21 @@ void gdn_lowrank_kernel(LowrankArgs a) {
 typedef __bf16 lr_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float lr_f32x4 __attribute__((ext_vector_type(4)));
 
+// Two floats as three bf16 parts each (hi, mid, lo: truncations of the value and of the two
+// remainders), packed in pairs (x in the low half); hi + mid + lo is exactly the value (24
+// significant bits in three runs of 8), so products of exact bf16 operands with the three
+// parts sum to the fp32 product.
+__device__ __forceinline__ void lr_split3(float x, float y, uint32_t& h, uint32_t& m, uint32_t& l) {
+    constexpr uint32_t HI = 0xffff0000u;
+    const uint32_t ux = __float_as_uint(x), uy = __float_as_uint(y);
+    const float rx = x - __uint_as_float(ux & HI), ry = y - __uint_as_float(uy & HI);
+    const uint32_t vx = __float_as_uint(rx), vy = __float_as_uint(ry);
+    const float sx = rx - __uint_as_float(vx & HI), sy = ry - __uint_as_float(vy & HI);
+    h = __builtin_amdgcn_perm(uy, ux, 0x07060302u);
+    m = __builtin_amdgcn_perm(vy, vx, 0x07060302u);
+    l = __builtin_amdgcn_perm(__float_as_uint(sy), __float_as_uint(sx), 0x07060302u);
+}
+
 // C += A B over a 16 x 16 x 32 slice, bf16 operands (lane l holds k = 8 (l/16) .. + 7 of its
 // row / column l % 16), fp32 accumulation into C[4 (l/16) + i][l % 16].
 __device__ __forceinline__ lr_f32x4 lr_mfma_k32(lr_u32x4 a, lr_u32x4 b, lr_f32x4 c) {
@@ -463,19 +478,24 @@ __device__ __forceinline__ lr_f32x4 lr_mfma4(float a, float b, lr_f32x4 c) {
 // each wave computing them for every slot (the waves need every slot's totals for their write
 // columns), which removes the per-token key FMAs, slot sums and the per-token exchange and
 // barrier of the vector form. The per-token pass over the write columns is the vector form's.
-template <int R>
+template <int R, typename ST>
 __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
     constexpr int D = 128;
     using AT = uint16_t;
-    using ST = uint16_t;
     using G = LrGeo<D, R, AT, ST>;
-    static_assert(G::W == 2 && G::EU == 2 && G::SG == 2 && (R == 16 || R == 32), "layout");
+    constexpr bool F32 = std::is_same<ST, float>::value;
+    static_assert(G::W == 2 && (R == 16 || R == 32) && (F32 || std::is_same<ST, uint16_t>::value),
+                  "layout");
     constexpr int DW = G::DW, SG = G::SG, RS = G::RS, EU = G::EU, CL = G::CL;
     constexpr int NTL = R / 16;     // 16-slot tiles of the key products
     constexpr int TS = kLrRound;    // tokens per round
     static_assert(TS == 8, "a round's k and q fill the 16 product columns");
-    constexpr int KST = D / 2 + 4;  // row stride (words) of staged keys: rows in other banks
-    __shared__ alignas(16) uint32_t ks[R][KST];              // the window's keys (bf16 pairs)
+    constexpr int KST = D / 2 + 4;  // row stride (words) of staged bf16 rows: rows in other banks
+    // The window's keys: a bf16 window's as raw bf16 pairs, an fp32 window's as floats (split
+    // exactly into three bf16 parts where they enter the products).
+    constexpr int KW = F32 ? D + 4 : KST;                    // words per key row
+    constexpr int KCR = D * (int)sizeof(ST) / 16;            // 16-byte chunks per key row
+    __shared__ alignas(16) uint32_t ks[R][KW];
     __shared__ alignas(16) uint32_t kq_raw[2][TS][KST];      // the round's k and q (bf16 pairs)
     __shared__ alignas(16) float vs[TS][D];                  // the round's v
     __shared__ float tok_ab[2][TS];                          // [alpha, beta][token]
@@ -521,12 +541,13 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
     };
     stage_loads(0);
     // The window's keys in LDS, one copy per head (thread tid moves 16-byte chunks
-    // tid + 128 j: slot chunk / 16, columns 8 (chunk % 16) .. + 7).
-    lr_u32x4 kc[R / 8];
+    // tid + 128 j: slot chunk / KCR, words 4 (chunk % KCR) .. + 3 of the row).
+    constexpr int KCT = R * KCR / 128;                       // chunks per thread
+    lr_u32x4 kc[KCT];
 #pragma unroll
-    for (int j = 0; j < R / 8; ++j) {
-        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
-        kc[j] = __builtin_nontemporal_load((const lr_u32x4*)(Kh + row * D + cw8));
+    for (int j = 0; j < KCT; ++j) {
+        const int chunk = tid + 128 * j, row = chunk / KCR, cw = (chunk % KCR) * 4;
+        kc[j] = __builtin_nontemporal_load((const lr_u32x4*)((const uint32_t*)(Kh + row * D) + cw));
     }
     float Ur[RS][EU];
 #pragma unroll
@@ -537,9 +558,9 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
     const uint32_t p0 = (uint32_t)a.pos[head] & (uint32_t)(R - 1);
     uint32_t p = p0;
 #pragma unroll
-    for (int j = 0; j < R / 8; ++j) {
-        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
-        *(lr_u32x4*)&ks[row][cw8 / 2] = kc[j];
+    for (int j = 0; j < KCT; ++j) {
+        const int chunk = tid + 128 * j, row = chunk / KCR, cw = (chunk % KCR) * 4;
+        *(lr_u32x4*)&ks[row][cw] = kc[j];
     }
 
     for (int t0 = 0; t0 < T; t0 += TS) {
@@ -571,8 +592,27 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
             const lr_u32x4 bv = *(const lr_u32x4*)&kq_raw[mq >> 3][vn][wo];
             const lr_u32x4 av = *(const lr_u32x4*)&kq_raw[0][vn][wo];   // rows >= 8 unused
 #pragma unroll
-            for (int t = 0; t < NTL; ++t)
-                C[t] = lr_mfma_k32(*(const lr_u32x4*)&ks[16 * t + mq][wo], bv, C[t]);
+            for (int t = 0; t < NTL; ++t) {
+                if constexpr (F32) {
+                    // columns 8 gq + 32 s .. + 7 as floats, in three exact bf16 parts
+                    const lr_u32x4 x0 = *(const lr_u32x4*)&ks[16 * t + mq][2 * wo];
+                    const lr_u32x4 x1 = *(const lr_u32x4*)&ks[16 * t + mq][2 * wo + 4];
+                    const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    uint32_t hh[4], mm[4], ll[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        lr_split3(__uint_as_float(xs[2 * e]), __uint_as_float(xs[2 * e + 1]),
+                                  hh[e], mm[e], ll[e]);
+                    const lr_u32x4 ph = {hh[0], hh[1], hh[2], hh[3]};
+                    const lr_u32x4 pm = {mm[0], mm[1], mm[2], mm[3]};
+                    const lr_u32x4 pl = {ll[0], ll[1], ll[2], ll[3]};
+                    C[t] = lr_mfma_k32(ph, bv, C[t]);
+                    C[t] = lr_mfma_k32(pm, bv, C[t]);
+                    C[t] = lr_mfma_k32(pl, bv, C[t]);
+                } else {
+                    C[t] = lr_mfma_k32(*(const lr_u32x4*)&ks[16 * t + mq][wo], bv, C[t]);
+                }
+            }
             Cp = lr_mfma_k32(av, bv, Cp);
         }
         // lane (gq, n = mq) holds C[t][e] = K_{16t + 4gq + e} . w_n and Cp[e] = k_{t0+4gq+e} . w_n
@@ -639,9 +679,19 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
         }
         // The round's keys replace the slots it wrote (every key product of the round was
         // formed before the barrier that precedes the per-token pass).
-        if (su < nt)
-            *(lr_u32x4*)&ks[(pr + (uint32_t)su) & (uint32_t)(R - 1)][scol / 2] =
-                *(const lr_u32x4*)&kq_raw[0][su][scol / 2];
+        if (su < nt) {
+            const lr_u32x4 kr = *(const lr_u32x4*)&kq_raw[0][su][scol / 2];
+            uint32_t* dst = &ks[(pr + (uint32_t)su) & (uint32_t)(R - 1)][0];
+            if constexpr (F32) {
+                // the bf16 keys widen exactly
+                *(lr_u32x4*)(dst + scol) = lr_u32x4{kr.x << 16, kr.x & 0xffff0000u,
+                                                    kr.y << 16, kr.y & 0xffff0000u};
+                *(lr_u32x4*)(dst + scol + 4) = lr_u32x4{kr.z << 16, kr.z & 0xffff0000u,
+                                                        kr.w << 16, kr.w & 0xffff0000u};
+            } else {
+                *(lr_u32x4*)(dst + scol / 2) = kr;
+            }
+        }
     }
 
     // Store the slots this call wrote, every weight, and the next slot.
@@ -652,10 +702,10 @@ __global__ __launch_bounds__(128) void gdn_lowrank_mm_kernel(LowrankArgs a) {
             store_run<ST, EU>(Uh + (sg * RS + i) * D + uc, Ur[i]);
     __syncthreads();   // the last round's keys are in ks
 #pragma unroll
-    for (int j = 0; j < R / 8; ++j) {
-        const int chunk = tid + 128 * j, row = chunk >> 4, cw8 = (chunk & 15) * 8;
+    for (int j = 0; j < KCT; ++j) {
+        const int chunk = tid + 128 * j, row = chunk / KCR, cw = (chunk % KCR) * 4;
         if ((((uint32_t)row - p0) & (uint32_t)(R - 1)) < written)
-            *(lr_u32x4*)(Kh + row * D + cw8) = *(const lr_u32x4*)&ks[row][cw8 / 2];
+            *(lr_u32x4*)((uint32_t*)(Kh + row * D) + cw) = *(const lr_u32x4*)&ks[row][cw];
     }
     if (w == 0) {
         if (lane % CL == 0) {
@@ -987,7 +1037,15 @@ hipError_t launch_typed(const LowrankArgs& a, hipStream_t stream) {
         // bf16 window and activations: several tokens take the matrix-core key products, and
         // rounds that are full or nearly so run in matrix form
         if (lr_round_form(a.T)) fn = (const void*)gdn_lowrank_round_kernel<R>;
-        else if (a.T > 1) fn = (const void*)gdn_lowrank_mm_kernel<R>;
+        else if (a.T > 1) fn = (const void*)gdn_lowrank_mm_kernel<R, ST>;
+    }
+    if constexpr (D == 128 && R == 16 && std::is_same<AT, uint16_t>::value &&
+                  std::is_same<ST, float>::value) {
+        // 16-slot fp32 window, bf16 activations: from 4 tokens on, the matrix-core key
+        // products (the keys in three exact bf16 parts). B = 256, H = 48, against the vector
+        // form: T = 2 41.3 -> 43.5 us (kept on the vector form), T = 4 56.2 -> 53.6, T = 6
+        // 79.2 -> 72.3.
+        if (a.T >= 4) fn = (const void*)gdn_lowrank_mm_kernel<R, ST>;
     }
     return hipLaunchKernel(fn, dim3((uint32_t)heads), dim3(64 * G::W), argv, 0, stream);
 }

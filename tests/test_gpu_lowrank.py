@@ -73,13 +73,16 @@ def test_single_stream_workload_all_heads(sdt):
 
 def test_split_calls_equal_one_call_bitwise():
     # fp32 state: a call boundary stores and reloads exact values, so T tokens in one call and
-    # the same tokens over three calls agree bit for bit.
+    # the same tokens over two calls of 4 and 5 tokens agree bit for bit (each token's
+    # arithmetic does not depend on how the call groups the tokens into rounds). Calls of fewer
+    # than 4 tokens on an fp32 window take the vector kernel, whose key sums round
+    # differently: see the next test.
     _announce("lowrank split calls B=2 H=5 D=128 r=16 T=9")
     x = synth.lowrank_inputs(2, 5, 128, 9, 16, act="bf16", seed=11)
     g1, o1 = gpu_lowrank(x)
     g2 = to_dev(x)
     outs = []
-    for a, z in ((0, 4), (4, 5), (5, 9)):
+    for a, z in ((0, 4), (4, 9)):
         sl = slice(a, z)
         outs.append(gdn.lowrank_decode_step(*(g2[n][:, sl].contiguous()
                                               for n in ("q", "k", "v", "alpha", "beta")),
@@ -88,6 +91,26 @@ def test_split_calls_equal_one_call_bitwise():
     assert torch.equal(o1, torch.cat(outs, dim=1))
     for n in LOWRANK_STATE:
         assert torch.equal(g1[n], g2[n]), n
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_split_calls_with_single_tokens_match_the_oracle(sdt):
+    # Calls of 4, 1 and 4 tokens (the single-token call on the vector kernel, the others on the
+    # matrix-core key products), each against the oracle run from the window the previous call
+    # stored.
+    _announce(f"lowrank split calls with a single token state={sdt}")
+    x = synth.lowrank_inputs(2, 5, 128, 9, 16, act="bf16", state_dtype=sdt, seed=12)
+    g = to_dev(x)
+    win = {n: x[n] for n in LOWRANK_STATE}
+    for a, z in ((0, 4), (4, 5), (5, 9)):
+        part = {n: x[n][:, a:z].contiguous() for n in ("q", "k", "v", "alpha", "beta")}
+        o = gdn.lowrank_decode_step(*(g[n][:, a:z].contiguous()
+                                      for n in ("q", "k", "v", "alpha", "beta")),
+                                    g["U"], g["K"], g["c"], g["pos"])
+        torch.cuda.synchronize()
+        ref = oracle_lowrank(dict(part, **win))
+        check_lowrank({n: g[n] for n in LOWRANK_STATE}, o, ref, torch.bfloat16, DT[sdt])
+        win = {n: g[n].cpu() for n in LOWRANK_STATE}
 
 
 def test_pos_is_read_modulo_r():
