@@ -12,8 +12,8 @@ import torch
 import gated_deltanet_recurrent_02_amd as gdn
 import oracle
 from gated_deltanet_recurrent_02_amd import synth
-from parity import (check_o, check_state, f64, gpu_decode, oracle_decode, oracle_decode_all,
-                    sample_heads, to_dev)
+from parity import (check_o, check_state, f64, gpu_decode, head_rel_err, oracle_decode,
+                    oracle_decode_all, sample_heads, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -335,3 +335,44 @@ def test_16bit_state_store_rounds_to_nearest_even(sdt):
     gn, wn = torch.isnan(got.float()), torch.isnan(want.float())
     assert torch.equal(gn, wn)
     assert torch.equal(got[~gn].view(torch.int16), want[~wn].view(torch.int16))
+
+
+GROWTH_STEPS = (16, 64, 256, 512)
+
+
+def test_16bit_state_error_growth_at_alpha_near_one():
+    # A decode loop stores the state after every token. With alpha close to 1 (alpha shift -6:
+    # alpha ~ 0.9975) little decays the rounding each store leaves, so the stored state drifts
+    # from the exact one like a random walk, of order sqrt(n) times the storage type's rounding
+    # after n stores. 512 single-token calls per state type from a zero state, compared at
+    # checkpoints with the fp64 oracle over the same tokens (which never rounds). Bars: fp32
+    # stays within 1e-5; each 16-bit type within 4 sqrt(n) of its rounding unit (2^-9 for bf16,
+    # 2^-12 for fp16); fp16 at least 4 times closer than bf16 at every checkpoint.
+    B, H, D, n = 2, 4, 128, GROWTH_STEPS[-1]
+    _announce(f"16-bit state error growth B={B} H={H} D={D} steps={n}")
+    x = synth.decode_inputs(B, H, D, n, act="bf16", state_dtype="f32", alpha_shift=-6.0,
+                            state_std=0.0, seed=61)
+    refs = {}
+    for c in GROWTH_STEPS:
+        part = {k: (v[:, :c].contiguous() if k in ("q", "k", "v", "alpha", "beta") else v)
+                for k, v in x.items()}
+        refs[c], _ = oracle_decode(part)
+    g = to_dev(x)
+    toks = [[g[k][:, t:t + 1].contiguous() for k in ("q", "k", "v", "alpha", "beta")]
+            for t in range(n)]
+    err = {}
+    for sdt in ("f32", "bf16", "f16"):
+        st = torch.zeros((B, H, D, D), dtype=DT[sdt], device="cuda")
+        for t in range(n):
+            gdn.decode_step(*toks[t], st)
+            if t + 1 in refs:
+                torch.cuda.synchronize()
+                err[(sdt, t + 1)] = head_rel_err(f64(st), refs[t + 1], 2)
+    print("\n[growth] steps " + " ".join(f"{c:>9d}" for c in GROWTH_STEPS))
+    for sdt in ("f32", "bf16", "f16"):
+        print(f"[growth] {sdt:>5} " + " ".join(f"{err[(sdt, c)]:9.2e}" for c in GROWTH_STEPS))
+    for c in GROWTH_STEPS:
+        assert err[("f32", c)] <= 1e-5, (c, err[("f32", c)])
+        assert err[("bf16", c)] <= 4 * np.sqrt(c) * 2.0 ** -9, (c, err[("bf16", c)])
+        assert err[("f16", c)] <= 4 * np.sqrt(c) * 2.0 ** -12, (c, err[("f16", c)])
+        assert 4 * err[("f16", c)] <= err[("bf16", c)], (c, err[("f16", c)], err[("bf16", c)])
