@@ -380,6 +380,23 @@ gdn_status prefill_impl(const char* fn, int64_t B, int32_t T, int32_t H, int32_t
         if (s != GDN_OK) return s;
     }
 
+    // Prompts shorter than kPrefillMinTokens run token by token on the decode kernel: the same
+    // result (the recurrence itself; no chunk records), and faster there at every batch size
+    // and state type measured on MI355X (e.g. B = 256, T = 8, fp32 state: 333 vs 509 us).
+    if (T < gdn::kPrefillMinTokens) {
+        gdn::DecodeArgs d;
+        d.B = B; d.T = T; d.H = H; d.D = dk;
+        d.q = q; d.k = k; d.v = v;
+        d.act = to_dtype(act_dtype);
+        d.alpha = alpha; d.beta = beta;
+        d.state = state;
+        d.state_dtype = to_dtype(state_dtype);
+        d.o = o; d.scale = scale;
+        hipError_t e = gdn::launch_decode(d, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail_hip((std::string(fn) + ": kernel launch").c_str(), e);
+        return GDN_OK;
+    }
+
     gdn::PrefillArgs a;
     a.B = B; a.T = T; a.H = H; a.D = dk;
     a.q = q; a.k = k; a.v = v; a.act = to_dtype(act_dtype);

@@ -195,8 +195,9 @@ gdn_status gdn_prefill_workspace_size(int64_t B, int32_t T, int32_t H, int32_t d
  *   workspace_bytes  its size in bytes
  * Errors: as gdn_decode_step; GDN_ERR_INVALID_ARGUMENT also for a workspace smaller than
  * required; GDN_ERR_UNSUPPORTED when B * H * ceil(T / 16) * 64 >= 2^32 (the prep kernel's
- * single dispatch). For runs of fewer than 16 tokens gdn_decode_step is faster; this call
- * always runs the chunked form.
+ * single dispatch). Runs of fewer than 16 tokens take gdn_decode_step's kernel instead (the
+ * same recurrence, faster there; the workspace is then not touched, and the non-finite caveat
+ * above does not apply).
  */
 gdn_status gdn_prefill(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                        const void* q, const void* k, const void* v, gdn_dtype act_dtype,

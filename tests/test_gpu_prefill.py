@@ -317,3 +317,27 @@ def test_graph_capture_of_a_long_prompt():
         gdn.prefill(y["q"], y["k"], y["v"], y["alpha"], y["beta"], y["state"], workspace=ws)
         torch.cuda.synchronize()
         check_state(f64(y["state"]), S_ref, torch.float32, what=f"eager state after replay {rep}")
+
+
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 7, 15])
+def test_short_prompts_take_the_decode_kernel(sdt, T):
+    # Fewer than 16 tokens run on gdn_decode_step's kernel: bit-identical results, and the
+    # workspace (filled with NaN) is left as it was.
+    _announce(f"prefill short prompt T={T} state={sdt}")
+    x = synth.decode_inputs(3, 5, 128, T, act="bf16", state_dtype=sdt, alpha_shift=-1.0,
+                            state_std=0.3, seed=90 + T)
+    g, d = to_dev(x), to_dev(x)
+    ws = gdn.prefill_workspace(g["q"], g["v"])
+    ws.view(torch.uint8).fill_(0xFF)
+    before = ws.clone()
+    tok = ("q", "k", "v", "alpha", "beta")
+    o1 = gdn.prefill(*(g[n] for n in tok), g["state"], workspace=ws)
+    o2 = gdn.decode_step(*(d[n] for n in tok), d["state"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(g["state"].view(torch.uint8), d["state"].view(torch.uint8))
+    assert torch.equal(ws, before)
+    S_ref, o_ref = oracle_decode(x)
+    check_state(f64(g["state"]), S_ref, DT[sdt])
+    check_o(f64(o1), o_ref, torch.bfloat16)
