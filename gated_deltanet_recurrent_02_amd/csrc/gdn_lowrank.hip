@@ -22,10 +22,11 @@
 // per token; at D = 64 two waves share a head; below, one wave holds a whole head. Every wave
 // keeps its share of the window in registers for all T tokens of the call.
 // Only the slots the call wrote (one per token; all of them once T >= r) are stored back.
-// Multi-token calls on a bf16 window with bf16 activations at D = 128 run
-// gdn_lowrank_mm_kernel instead, which forms each round's key products on the matrix cores, or
-// (when its rounds are full or nearly so, lr_round_form) gdn_lowrank_round_kernel, which takes
-// each round of tokens in matrix form on the matrix cores (see there).
+// Multi-token calls with bf16 activations at D = 128 on a bf16 window (and on a 16-slot fp32
+// window from 4 tokens on) run gdn_lowrank_mm_kernel instead, which forms each round's key
+// products on the matrix cores, or, on a bf16 window whose rounds are full or nearly so
+// (lr_round_form), gdn_lowrank_round_kernel, which takes each round of tokens in matrix form on
+// the matrix cores (see there).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -465,8 +466,9 @@ __device__ __forceinline__ lr_f32x4 lr_mfma4(float a, float b, lr_f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Multi-token calls on a bf16 window with bf16 activations at D = 128 (r = 16 or 32): the key
-// products of a whole round run on the matrix cores instead of per token on the vector ALUs.
+// Multi-token calls with bf16 activations at D = 128 on a bf16 window (r = 16 or 32) or a
+// 16-slot fp32 window: the key products of a whole round run on the matrix cores instead of
+// per token on the vector ALUs (an fp32 window's keys as three exact bf16 parts each).
 // Both operands are exact bf16 and the products accumulate in fp32, as in the vector form
 // (summation order differs). Per round of up to kLrRound tokens t0 .. t0+nt-1 (window slot p_r
 // the next to be written at the round's start):

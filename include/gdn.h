@@ -253,7 +253,10 @@ gdn_status gdn_prefill_noalloc(int64_t B, int32_t T, int32_t H, int32_t dk, int3
  *                                     written back as (pos + T) mod r
  * Within one call U, K and c stay fp32 in registers; only the slots the call wrote (one per
  * token, all r once T >= r), every weight and pos are stored. Stores to a 16-bit state round to
- * nearest even once per call. Non-finite inputs stay within their own (b, h).
+ * nearest even once per call. Non-finite inputs stay within their own (b, h); where a call on
+ * a bf16 window (bf16 activations, D = 128, T >= 8 with T mod 8 in {0, 6, 7}) takes its tokens
+ * in rounds of 8 in matrix form, a NaN or infinity in a token's k, q or v can also reach the
+ * earlier outputs of its own round.
  * Errors: as gdn_decode_step; U, K, c and pos must not overlap each other or the inputs, and o
  * must not overlap any argument (GDN_ERR_INVALID_ARGUMENT).
  */
