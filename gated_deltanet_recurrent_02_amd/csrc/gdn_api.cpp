@@ -325,6 +325,11 @@ namespace {
 
 // gdn_prefill and gdn_prefill_noalloc: validation, then the launch with the given workspace.
 // `workspace` NULL means the library's fixed device scratch (no allocation, no caller buffer).
+// Prompts of fewer tokens than this take the token-by-token decode kernel instead of the
+// chunked form (measured faster for T <= 12 at B = 1, 32 and 256 with fp32 and bf16 states,
+// slower from T = 16 on except where the two are within 5%).
+constexpr int32_t kPrefillMinTokens = 16;
+
 gdn_status prefill_impl(const char* fn, int64_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                         const void* q, const void* k, const void* v, gdn_dtype act_dtype,
                         const float* alpha, const float* beta, void* state, gdn_dtype state_dtype,
@@ -383,7 +388,7 @@ gdn_status prefill_impl(const char* fn, int64_t B, int32_t T, int32_t H, int32_t
     // Prompts shorter than kPrefillMinTokens run token by token on the decode kernel: the same
     // result (the recurrence itself; no chunk records), and faster there at every batch size
     // and state type measured on MI355X (e.g. B = 256, T = 8, fp32 state: 333 vs 509 us).
-    if (T < gdn::kPrefillMinTokens) {
+    if (T < kPrefillMinTokens) {
         gdn::DecodeArgs d;
         d.B = B; d.T = T; d.H = H; d.D = dk;
         d.q = q; d.k = k; d.v = v;

@@ -16,10 +16,6 @@ namespace gdn {
 //   [512, 528) gamma_t: alpha_0 ... alpha_t (alpha = 1 past the end of the sequence)
 //   [528, 544) Gam_end,t: alpha_{t+1} ... alpha_15
 constexpr int kPrefillChunk = 16;
-// Prompts of fewer tokens than this take the token-by-token decode kernel instead (measured
-// faster for T <= 12 at B = 1, 32 and 256 with fp32 and bf16 states, slower from T = 16 on
-// except where the two are within 5%).
-constexpr int kPrefillMinTokens = 16;
 constexpr int kPrefillRecordFloats = 544;
 
 struct PrefillArgs {
