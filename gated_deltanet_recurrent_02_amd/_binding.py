@@ -88,14 +88,26 @@ def check(status: int) -> None:
 
 
 def _ptr(t: torch.Tensor | None):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+# The current stream's raw handle without building a torch.cuda.Stream object (1.7 us per call
+# from Python on the MI355X host; the raw accessor takes 0.1 us); torch builds without it take
+# the public accessor.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(dev: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _need(t: torch.Tensor, name: str, shape: tuple, dtypes: tuple) -> None:
+    # one combined test on the common path, the specific message only when it fails
+    if (isinstance(t, torch.Tensor) and t.dtype in dtypes and t.shape == shape and t.is_cuda
+            and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
@@ -104,8 +116,7 @@ def _need(t: torch.Tensor, name: str, shape: tuple, dtypes: tuple) -> None:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    raise ValueError(f"{name} must be contiguous")
 
 
 _ACT = (torch.float32, torch.bfloat16, torch.float16)
