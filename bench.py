@@ -79,6 +79,10 @@ PROBE_LIBRARY = os.path.join(_PKG, "libgdn_probe.so")
 # Extra workloads timed with the default one: (label, workload, state dtype).
 EXTRA_CONFIGS = [
     ("single_stream_b1_f32", "decode_b1_h48_d128_t1", "f32"),
+    # the same single stream over 48 layers (one token's pass through a 48-layer model: 151 MB
+    # of state, which the 256 MB MALL can hold) and hot (one layer, cache-resident), labelled
+    ("single_stream_b1_f32_48_layers", "decode_b1_h48_d128_t1", "f32", {"layers": 48}),
+    ("single_stream_b1_f32_hot", "decode_b1_h48_d128_t1", "f32", {"layers": 1}),
     ("mid_batch_b64_f32", "decode_b64_h48_d128_t1", "f32"),
     ("bottleneck_b256_bf16_state", "decode_b256_h48_d128_t1", "bf16"),
     ("fused_b256_t4_f32", "fused_b256_h48_d128_t4", "f32"),
