@@ -671,6 +671,298 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
     store_state<G>(Sg, rbase + g, l, S);
 }
 
+// ------------------------------------------------------------------------ chunk-form decode
+
+// A few tokens (2 .. TCH) on a bf16 state with bf16 activations. The token-by-token form needs
+// S_{t-1} k_t and S_t q_t, two FMAs per state element and token on the current fp32 state. Over
+// one call they unroll to products with the stored state S0 (the chunk form of the same
+// recurrence; "GDN tuning limits on Kunlun XPU", section 三.3 names it):
+//     gamma_t = alpha_0 ... alpha_t,  d(t, s) = alpha_{s+1} ... alpha_t  (d(t, t) = 1),
+//     S_{t-1} k_t = gamma_{t-1} S0 k_t + sum_{s<t} d(t-1, s) (k_s . k_t) delta_s,
+//     delta_t = beta_t (v_t - alpha_t S_{t-1} k_t),
+//     o_t = scale (gamma_t S0 q_t + sum_{s<=t} d(t, s) (k_s . q_t) delta_s),
+//     S_T = gamma_{T-1} S0 + sum_s d(T-1, s) delta_s k_s^T.
+// S0 is the loaded bf16 state and k, q are bf16, so S0 k_t and S0 q_t take one packed bf16 dot
+// (v_dot2c_f32_bf16: two products, fp32 accumulation) per two elements on the raw words, with
+// no widening; the Gram products k_s . k_t, k_s . q_t are shared by the workgroup through LDS,
+// the decays are running products of alpha, and the per-row part is a few scalar operations
+// per token; the state is widened, updated and rounded once at the end.
+
+template <int D, int TCH>
+struct ChunkLds {
+    alignas(16) uint16_t kb[TCH][D];  // k, q as stored (bf16 bits)
+    alignas(16) uint16_t qb[TCH][D];
+    alignas(16) float k[TCH][D];      // k widened (the final update)
+    alignas(16) float v[TCH][D];      // v widened (the workgroup's rows)
+    float alpha[TCH], beta[TCH];
+    float kk[TCH][TCH];               // k_s . k_t
+    float kq[TCH][TCH];               // k_s . q_t
+};
+
+typedef __bf16 bf16x2_dot_t __attribute__((ext_vector_type(2)));
+
+// acc + x.lo y.lo + x.hi y.hi for two packed bf16 pairs (fp32 accumulation).
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_dot_t, x),
+                                           __builtin_bit_cast(bf16x2_dot_t, y), acc, false);
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
+    int T, int H, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, uint16_t* __restrict__ state, uint16_t* __restrict__ o,
+    float scale) {
+    constexpr int D = G::D, TCH = G::TCH, E = G::E, P = G::P, W = E / 2;
+    static_assert(sizeof(typename G::ST) == 2 && E % 2 == 0 && G::SPLIT == 1, "bf16 rows");
+    static_assert(TCH * TCH <= 64, "one lane per token pair");
+    __shared__ ChunkLds<D, TCH> L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / G::LPR, l = lane % G::LPR;
+    const uint32_t tile = tile_index<G::GRP>(blockIdx.x, gridDim.x);
+    const int64_t n = tile;  // b * H + h
+    const int64_t b = n / H;
+    const int h = (int)(n - b * H);
+    uint16_t* Sg = state + (size_t)n * D * D;
+    const int rbase = wave * G::RPW;
+    const int nt = T;  // 2 .. TCH, checked by the launcher
+
+    // ---- stage the tokens (fetch before the state loads), load the state as stored
+    constexpr int CHK = 8;                       // bf16 per 16-byte chunk
+    constexpr int NQ = D / CHK;                  // chunks of q (= of k, = of v)
+    constexpr int NCHK = 3 * NQ;                 // chunks per token
+    constexpr int CPL = (TCH * NCHK + G::NT - 1) / G::NT;
+    static_assert(D % CHK == 0, "whole 16-byte chunks");
+    u32x4 raw[CPL];
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) {
+        const int c = tid + s * G::NT;
+        if (c < nt * NCHK) {
+            const int tt = c / NCHK, r = c - tt * NCHK;
+            const size_t tok = ((size_t)b * T + tt) * H + h;
+            const uint16_t* src = r < NQ ? q + tok * D + r * CHK
+                                : r < 2 * NQ ? k + tok * D + (r - NQ) * CHK
+                                             : v + tok * D + (r - 2 * NQ) * CHK;
+            raw[s] = *(const u32x4*)src;
+        }
+    }
+    float al = 0.f, be = 0.f;
+    if (tid < nt) {
+        const size_t tok = ((size_t)b * T + tid) * H + h;
+        al = alpha[tok];
+        be = beta[tok];
+    }
+    uint32_t Sw[P][W];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint16_t* rowp = Sg + (size_t)(rbase + g + p * G::RPP) * D;
+#pragma unroll
+        for (int c = 0; c < G::NCH; ++c) {
+            Words<G::VB> w = gload<G::VB, G::NTL>(rowp + c * G::LPR * G::VW + l * G::VW);
+#pragma unroll
+            for (int i = 0; i < G::VW / 2; ++i) Sw[p][c * (G::VW / 2) + i] = w.w[i];
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) {
+        const int c = tid + s * G::NT;
+        if (c < nt * NCHK) {
+            const int tt = c / NCHK, r = c - tt * NCHK;
+            const uint32_t wv[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+            if (r < 2 * NQ) {
+                uint16_t* dst = r < NQ ? &L.qb[tt][r * CHK] : &L.kb[tt][(r - NQ) * CHK];
+                *(u32x4*)dst = raw[s];
+            }
+            if (r >= NQ) {
+                float* dst = r < 2 * NQ ? &L.k[tt][(r - NQ) * CHK] : &L.v[tt][(r - 2 * NQ) * CHK];
+                *(float4*)dst = make_float4(bf16_to_f32(wv[0] & 0xffffu), __uint_as_float(wv[0] & 0xffff0000u),
+                                            bf16_to_f32(wv[1] & 0xffffu), __uint_as_float(wv[1] & 0xffff0000u));
+                *(float4*)(dst + 4) = make_float4(bf16_to_f32(wv[2] & 0xffffu), __uint_as_float(wv[2] & 0xffff0000u),
+                                                  bf16_to_f32(wv[3] & 0xffffu), __uint_as_float(wv[3] & 0xffff0000u));
+            }
+        }
+    }
+    if (tid < nt) {
+        L.alpha[tid] = al;
+        L.beta[tid] = be;
+    }
+    __syncthreads();
+
+    // ---- Gram products k_s . k_t and k_s . q_t over the workgroup: token pair (s, t) =
+    // (pi / TCH, pi % TCH) on the LG = NT / TCH^2 lanes of group pi = tid / LG, each lane
+    // summing D / LG columns; the pairs reach LDS for every wave.
+    {
+        constexpr int LG = G::NT / (TCH * TCH);  // lanes per pair
+        constexpr int CW = D / LG / 2;           // words per lane
+        static_assert(G::NT % (TCH * TCH) == 0 &&
+                      (LG == 1 || LG == 2 || LG == 4 || LG == 8 || LG == 16) && CW % 4 == 0,
+                      "Gram lanes");
+        const int pi = tid / LG, j = tid % LG;
+        const int gs = pi / TCH, gt = pi % TCH;
+        const u32x4* ks = (const u32x4*)&L.kb[gs][2 * CW * j];
+        const u32x4* kt = (const u32x4*)&L.kb[gt][2 * CW * j];
+        const u32x4* qt = (const u32x4*)&L.qb[gt][2 * CW * j];
+        float a = 0.f, c = 0.f;
+        if (gs < nt && gt < nt) {
+#pragma unroll
+            for (int w = 0; w < CW / 4; ++w) {
+                const u32x4 x = ks[w], y = kt[w], z = qt[w];
+                a = dot2_bf16(x.x, y.x, a); a = dot2_bf16(x.y, y.y, a);
+                a = dot2_bf16(x.z, y.z, a); a = dot2_bf16(x.w, y.w, a);
+                c = dot2_bf16(x.x, z.x, c); c = dot2_bf16(x.y, z.y, c);
+                c = dot2_bf16(x.z, z.z, c); c = dot2_bf16(x.w, z.w, c);
+            }
+        }
+        if constexpr (LG >= 2) {
+            a += dpp_mov<0xB1>(a);
+            c += dpp_mov<0xB1>(c);
+        }
+        if constexpr (LG >= 4) {
+            a += dpp_mov<0x4E>(a);
+            c += dpp_mov<0x4E>(c);
+        }
+        if constexpr (LG >= 8) {
+            a += dpp_mov<0x141>(a);
+            c += dpp_mov<0x141>(c);
+        }
+        if constexpr (LG >= 16) {
+            a += dpp_mov<0x140>(a);
+            c += dpp_mov<0x140>(c);
+        }
+        if (j == 0) {
+            L.kk[gs][gt] = a;
+            L.kq[gs][gt] = c;
+        }
+    }
+    __syncthreads();
+
+    // ---- tokens: S0 k_t and S0 q_t on the stored words, then the per-row recurrence. The
+    // per-head coefficients are formed inline (wave-uniform values): dc[s] = d(t, s) and
+    // dp[s] = d(t-1, s) as running products, gam = gamma_t, gprev = gamma_{t-1}.
+    float dl[P][TCH];  // delta_s of the lane's rows
+    float dc[TCH];
+    float gam = 1.0f;
+    const size_t ostride = (size_t)H * D;
+    uint16_t* obase = o + ((size_t)b * T * H + h) * D;
+#pragma unroll
+    for (int t = 0; t < TCH; ++t) {
+        if (t >= nt) break;
+        const float at = L.alpha[t], bt = L.beta[t];
+        const float gprev = gam;
+        gam *= at;
+        float dp[TCH];
+#pragma unroll
+        for (int s = 0; s < TCH; ++s) {
+            if (s < t) {
+                dp[s] = dc[s];
+                dc[s] = s < t - 1 ? dc[s] * at : at;
+            }
+        }
+        dc[t] = 1.0f;
+        if (t > 0) dp[t - 1] = 1.0f;
+        uint32_t kw[W], qw[W];
+#pragma unroll
+        for (int c = 0; c < G::NCH; ++c) {
+            const int col = c * G::LPR * G::VW + l * G::VW;
+            Words<G::VB> a = gload<G::VB, false>(&L.kb[t][col]);
+            Words<G::VB> bq = gload<G::VB, false>(&L.qb[t][col]);
+#pragma unroll
+            for (int i = 0; i < G::VW / 2; ++i) {
+                kw[c * (G::VW / 2) + i] = a.w[i];
+                qw[c * (G::VW / 2) + i] = bq.w[i];
+            }
+        }
+        float u0[P], w0[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            float su = 0.f, sw = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                su = dot2_bf16(Sw[p][w], kw[w], su);
+                sw = dot2_bf16(Sw[p][w], qw[w], sw);
+            }
+            u0[p] = su;
+            w0[p] = sw;
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            u0[p] = row_sum<G::LPR>(u0[p]);
+            w0[p] = row_sum<G::LPR>(w0[p]);
+        }
+        float cu[TCH], co[TCH];
+#pragma unroll
+        for (int s = 0; s < TCH; ++s) {
+            if (s < t) cu[s] = dp[s] * L.kk[s][t];
+            if (s <= t) co[s] = dc[s] * L.kq[s][t];
+        }
+        float ov = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int row = rbase + g + p * G::RPP;
+            float u = gprev * u0[p];
+#pragma unroll
+            for (int s = 0; s < TCH; ++s)
+                if (s < t) u = fmaf(cu[s], dl[p][s], u);
+            dl[p][t] = bt * (L.v[t][row] - at * u);
+            float op = gam * w0[p];
+#pragma unroll
+            for (int s = 0; s < TCH; ++s)
+                if (s <= t) op = fmaf(co[s], dl[p][s], op);
+            ov = (l == p) ? scale * op : ov;
+        }
+        if (l < P) obase[(size_t)t * ostride + rbase + l * G::RPP + g] = act_from_f32<uint16_t>(ov);
+    }
+
+    // ---- S_T = gamma_{T-1} S0 + sum_s d(T-1, s) delta_s k_s^T, rounded once, stored
+    // after the last token dc[s] = d(T-1, s) and gam = gamma_{T-1}
+    const float gT = gam;
+    float cs[P][TCH];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int s = 0; s < TCH; ++s) cs[p][s] = s < nt ? dc[s] * dl[p][s] : 0.0f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        uint16_t* rowp = Sg + (size_t)(rbase + g + p * G::RPP) * D;
+#pragma unroll
+        for (int c = 0; c < G::NCH; ++c) {
+            const int col = c * G::LPR * G::VW + l * G::VW;
+            float acc[G::VW];
+#pragma unroll
+            for (int i = 0; i < G::VW; i += 2) {
+                const uint32_t wd = Sw[p][c * (G::VW / 2) + i / 2];
+                acc[i] = gT * bf16_to_f32(wd & 0xffffu);
+                acc[i + 1] = gT * __uint_as_float(wd & 0xffff0000u);
+            }
+#pragma unroll
+            for (int s = 0; s < TCH; ++s) {
+                if (s >= nt) break;
+                if constexpr (G::VW % 4 == 0) {
+#pragma unroll
+                    for (int i = 0; i < G::VW; i += 4) {
+                        const float4 k4 = *(const float4*)&L.k[s][col + i];
+                        acc[i] = fmaf(cs[p][s], k4.x, acc[i]);
+                        acc[i + 1] = fmaf(cs[p][s], k4.y, acc[i + 1]);
+                        acc[i + 2] = fmaf(cs[p][s], k4.z, acc[i + 2]);
+                        acc[i + 3] = fmaf(cs[p][s], k4.w, acc[i + 3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < G::VW; i += 2) {
+                        const float2 k2 = *(const float2*)&L.k[s][col + i];
+                        acc[i] = fmaf(cs[p][s], k2.x, acc[i]);
+                        acc[i + 1] = fmaf(cs[p][s], k2.y, acc[i + 1]);
+                    }
+                }
+            }
+            Words<G::VB> w;
+#pragma unroll
+            for (int i = 0; i < G::VW; i += 2) w.w[i / 2] = f32x2_to_bf16x2(acc[i], acc[i + 1]);
+            gstore<G::VB, G::NTS>(rowp + col, w);
+        }
+    }
+}
+
 // ------------------------------------------------------------------------ verify kernel
 
 // Speculative verify with a deferred commit. The stored state is the committed state as of the
@@ -926,6 +1218,23 @@ hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t s) {
                            dim3((unsigned)(a.B * a.H * G::SPLIT)), dim3(G::NT), args, 0, s);
 }
 
+template <class G>
+hipError_t launch_chunk_g(const DecodeArgs& a, hipStream_t s) {
+    int T = a.T, H = a.H;
+    const uint16_t* q = (const uint16_t*)a.q;
+    const uint16_t* k = (const uint16_t*)a.k;
+    const uint16_t* v = (const uint16_t*)a.v;
+    const float* alpha = a.alpha;
+    const float* beta = a.beta;
+    uint16_t* state = (uint16_t*)a.state;
+    uint16_t* o = (uint16_t*)a.o;
+    float scale = a.scale;
+    void* args[] = {&T, &H, &q, &k, &v, &alpha, &beta, &state, &o, &scale};
+    static_assert((int64_t)G::NT <= kThreadsPerHeadPerDim * G::D, "threads per head");
+    return hipLaunchKernel((const void*)gdn_decode_chunk_kernel<G>, dim3((unsigned)(a.B * a.H)),
+                           dim3(G::NT), args, 0, s);
+}
+
 template <class G, typename AT>
 hipError_t launch_verify_g(const VerifyArgs& a, hipStream_t s) {
     int T = a.T, H = a.H, Tp = a.Tp;
@@ -1021,6 +1330,11 @@ template <int D> struct DecodeTokens<D, float> {
     using G = Geo<D, float, 1, max_int(1, D / 16), 8, true, true, 2, 16>;
 };
 
+// Chunk form (bf16 state and activations, 2 .. TCH tokens): the multi-token geometry.
+template <int D> struct DecodeChunk {
+    using G = Geo<D, uint16_t, max_int(1, D / 16), 1, 8, true, true, 4, 8>;
+};
+
 template <int D, typename ST> struct VerifyTokens {  // 2-byte states
     using G = Geo<D, ST, max_int(1, D / 16), 1, 8, true, true, 4, 8>;
 };
@@ -1042,6 +1356,9 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
             return launch_decode_g<typename DecodeOneToken<D, ST>::G_small, false, AT>(a, s);
     }
     if (a.T == 1) return launch_decode_g<typename DecodeOneToken<D, ST>::G, false, AT>(a, s);
+    if constexpr (sizeof(ST) == 2 && !is_f16<ST>::value && sizeof(AT) == 2 && !is_f16<AT>::value) {
+        if (a.T <= DecodeChunk<D>::G::TCH) return launch_chunk_g<typename DecodeChunk<D>::G>(a, s);
+    }
     return launch_decode_g<typename DecodeTokens<D, ST>::G, true, AT>(a, s);
 }
 
