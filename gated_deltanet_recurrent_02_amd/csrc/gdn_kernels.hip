@@ -707,55 +707,80 @@ __device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t y, float acc) {
                                            __builtin_bit_cast(bf16x2_dot_t, y), acc, false);
 }
 
+// The per-token vectors of the workgroup's head moved to LDS: k and q as stored, k and v
+// widened, the gates. fetch() issues the global loads into registers (before the state loads)
+// and commit() writes them, as TokenStage does for the token-by-token kernels.
 template <class G>
-__global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
-    int T, int H, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ alpha,
-    const float* __restrict__ beta, uint16_t* __restrict__ state, uint16_t* __restrict__ o,
-    float scale) {
-    constexpr int D = G::D, TCH = G::TCH, E = G::E, P = G::P, W = E / 2;
-    static_assert(sizeof(typename G::ST) == 2 && E % 2 == 0 && G::SPLIT == 1, "bf16 rows");
-    static_assert(TCH * TCH <= 64, "one lane per token pair");
-    __shared__ ChunkLds<D, TCH> L;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane / G::LPR, l = lane % G::LPR;
-    const uint32_t tile = tile_index<G::GRP>(blockIdx.x, gridDim.x);
-    const int64_t n = tile;  // b * H + h
-    const int64_t b = n / H;
-    const int h = (int)(n - b * H);
-    uint16_t* Sg = state + (size_t)n * D * D;
-    const int rbase = wave * G::RPW;
-    const int nt = T;  // 2 .. TCH, checked by the launcher
-
-    // ---- stage the tokens (fetch before the state loads), load the state as stored
-    constexpr int CHK = 8;                       // bf16 per 16-byte chunk
-    constexpr int NQ = D / CHK;                  // chunks of q (= of k, = of v)
-    constexpr int NCHK = 3 * NQ;                 // chunks per token
-    constexpr int CPL = (TCH * NCHK + G::NT - 1) / G::NT;
-    static_assert(D % CHK == 0, "whole 16-byte chunks");
+struct ChunkStage {
+    static constexpr int D = G::D, TCH = G::TCH;
+    static constexpr int CHK = 8;             // bf16 per 16-byte chunk
+    static constexpr int NQ = D / CHK;        // chunks of q (= of k, = of v)
+    static constexpr int NCHK = 3 * NQ;       // chunks per token
+    static constexpr int CPL = (TCH * NCHK + G::NT - 1) / G::NT;
+    static_assert(D % CHK == 0 && G::SPLIT == 1, "whole 16-byte chunks, whole heads");
     u32x4 raw[CPL];
+    float al = 0.f, be = 0.f;
+
+    __device__ __forceinline__ void fetch(const uint16_t* __restrict__ q,
+                                          const uint16_t* __restrict__ k,
+                                          const uint16_t* __restrict__ v,
+                                          const float* __restrict__ alpha,
+                                          const float* __restrict__ beta, int64_t b, int T, int H,
+                                          int h, int nt, int tid) {
 #pragma unroll
-    for (int s = 0; s < CPL; ++s) {
-        const int c = tid + s * G::NT;
-        if (c < nt * NCHK) {
-            const int tt = c / NCHK, r = c - tt * NCHK;
-            const size_t tok = ((size_t)b * T + tt) * H + h;
-            const uint16_t* src = r < NQ ? q + tok * D + r * CHK
-                                : r < 2 * NQ ? k + tok * D + (r - NQ) * CHK
-                                             : v + tok * D + (r - 2 * NQ) * CHK;
-            raw[s] = *(const u32x4*)src;
+        for (int s = 0; s < CPL; ++s) {
+            const int c = tid + s * G::NT;
+            if (c < nt * NCHK) {
+                const int tt = c / NCHK, r = c - tt * NCHK;
+                const size_t tok = ((size_t)b * T + tt) * H + h;
+                const uint16_t* src = r < NQ ? q + tok * D + r * CHK
+                                    : r < 2 * NQ ? k + tok * D + (r - NQ) * CHK
+                                                 : v + tok * D + (r - 2 * NQ) * CHK;
+                raw[s] = *(const u32x4*)src;
+            }
+        }
+        if (tid < nt) {
+            const size_t tok = ((size_t)b * T + tid) * H + h;
+            al = alpha[tok];
+            be = beta[tok];
         }
     }
-    float al = 0.f, be = 0.f;
-    if (tid < nt) {
-        const size_t tok = ((size_t)b * T + tid) * H + h;
-        al = alpha[tok];
-        be = beta[tok];
-    }
-    uint32_t Sw[P][W];
+
+    __device__ __forceinline__ void commit(ChunkLds<D, TCH>& L, int nt, int tid) const {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const uint16_t* rowp = Sg + (size_t)(rbase + g + p * G::RPP) * D;
+        for (int s = 0; s < CPL; ++s) {
+            const int c = tid + s * G::NT;
+            if (c < nt * NCHK) {
+                const int tt = c / NCHK, r = c - tt * NCHK;
+                const uint32_t wv[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+                if (r < 2 * NQ) {
+                    uint16_t* dst = r < NQ ? &L.qb[tt][r * CHK] : &L.kb[tt][(r - NQ) * CHK];
+                    *(u32x4*)dst = raw[s];
+                }
+                if (r >= NQ) {
+                    float* dst = r < 2 * NQ ? &L.k[tt][(r - NQ) * CHK] : &L.v[tt][(r - 2 * NQ) * CHK];
+                    *(float4*)dst = make_float4(unpack<uint16_t>(wv[0], 0), unpack<uint16_t>(wv[0], 1),
+                                                unpack<uint16_t>(wv[1], 0), unpack<uint16_t>(wv[1], 1));
+                    *(float4*)(dst + 4) = make_float4(unpack<uint16_t>(wv[2], 0), unpack<uint16_t>(wv[2], 1),
+                                                      unpack<uint16_t>(wv[3], 0), unpack<uint16_t>(wv[3], 1));
+                }
+            }
+        }
+        if (tid < nt) {
+            L.alpha[tid] = al;
+            L.beta[tid] = be;
+        }
+    }
+};
+
+// The state rows of the lane as stored: Sw[p][w] holds columns col(l, 2w), col(l, 2w + 1) of
+// row row0 + p RPP.
+template <class G>
+__device__ __forceinline__ void load_state_words(const uint16_t* __restrict__ Sg, int row0, int l,
+                                                 uint32_t (&Sw)[G::P][G::E / 2]) {
+#pragma unroll
+    for (int p = 0; p < G::P; ++p) {
+        const uint16_t* rowp = Sg + (size_t)(row0 + p * G::RPP) * G::D;
 #pragma unroll
         for (int c = 0; c < G::NCH; ++c) {
             Words<G::VB> w = gload<G::VB, G::NTL>(rowp + c * G::LPR * G::VW + l * G::VW);
@@ -763,87 +788,88 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
             for (int i = 0; i < G::VW / 2; ++i) Sw[p][c * (G::VW / 2) + i] = w.w[i];
         }
     }
-#pragma unroll
-    for (int s = 0; s < CPL; ++s) {
-        const int c = tid + s * G::NT;
-        if (c < nt * NCHK) {
-            const int tt = c / NCHK, r = c - tt * NCHK;
-            const uint32_t wv[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
-            if (r < 2 * NQ) {
-                uint16_t* dst = r < NQ ? &L.qb[tt][r * CHK] : &L.kb[tt][(r - NQ) * CHK];
-                *(u32x4*)dst = raw[s];
-            }
-            if (r >= NQ) {
-                float* dst = r < 2 * NQ ? &L.k[tt][(r - NQ) * CHK] : &L.v[tt][(r - 2 * NQ) * CHK];
-                *(float4*)dst = make_float4(bf16_to_f32(wv[0] & 0xffffu), __uint_as_float(wv[0] & 0xffff0000u),
-                                            bf16_to_f32(wv[1] & 0xffffu), __uint_as_float(wv[1] & 0xffff0000u));
-                *(float4*)(dst + 4) = make_float4(bf16_to_f32(wv[2] & 0xffffu), __uint_as_float(wv[2] & 0xffff0000u),
-                                                  bf16_to_f32(wv[3] & 0xffffu), __uint_as_float(wv[3] & 0xffff0000u));
-            }
-        }
-    }
-    if (tid < nt) {
-        L.alpha[tid] = al;
-        L.beta[tid] = be;
-    }
-    __syncthreads();
+}
 
-    // ---- Gram products k_s . k_t and k_s . q_t over the workgroup: token pair (s, t) =
-    // (pi / TCH, pi % TCH) on the LG = NT / TCH^2 lanes of group pi = tid / LG, each lane
-    // summing D / LG columns; the pairs reach LDS for every wave.
-    {
-        constexpr int LG = G::NT / (TCH * TCH);  // lanes per pair
-        constexpr int CW = D / LG / 2;           // words per lane
-        static_assert(G::NT % (TCH * TCH) == 0 &&
-                      (LG == 1 || LG == 2 || LG == 4 || LG == 8 || LG == 16) && CW % 4 == 0,
-                      "Gram lanes");
-        const int pi = tid / LG, j = tid % LG;
-        const int gs = pi / TCH, gt = pi % TCH;
-        const u32x4* ks = (const u32x4*)&L.kb[gs][2 * CW * j];
-        const u32x4* kt = (const u32x4*)&L.kb[gt][2 * CW * j];
-        const u32x4* qt = (const u32x4*)&L.qb[gt][2 * CW * j];
-        float a = 0.f, c = 0.f;
-        if (gs < nt && gt < nt) {
+template <class G>
+__device__ __forceinline__ void store_state_words(uint16_t* __restrict__ Sg, int row0, int l,
+                                                  const uint32_t (&Sw)[G::P][G::E / 2]) {
 #pragma unroll
-            for (int w = 0; w < CW / 4; ++w) {
-                const u32x4 x = ks[w], y = kt[w], z = qt[w];
-                a = dot2_bf16(x.x, y.x, a); a = dot2_bf16(x.y, y.y, a);
-                a = dot2_bf16(x.z, y.z, a); a = dot2_bf16(x.w, y.w, a);
-                c = dot2_bf16(x.x, z.x, c); c = dot2_bf16(x.y, z.y, c);
-                c = dot2_bf16(x.z, z.z, c); c = dot2_bf16(x.w, z.w, c);
-            }
-        }
-        if constexpr (LG >= 2) {
-            a += dpp_mov<0xB1>(a);
-            c += dpp_mov<0xB1>(c);
-        }
-        if constexpr (LG >= 4) {
-            a += dpp_mov<0x4E>(a);
-            c += dpp_mov<0x4E>(c);
-        }
-        if constexpr (LG >= 8) {
-            a += dpp_mov<0x141>(a);
-            c += dpp_mov<0x141>(c);
-        }
-        if constexpr (LG >= 16) {
-            a += dpp_mov<0x140>(a);
-            c += dpp_mov<0x140>(c);
-        }
-        if (j == 0) {
-            L.kk[gs][gt] = a;
-            L.kq[gs][gt] = c;
+    for (int p = 0; p < G::P; ++p) {
+        uint16_t* rowp = Sg + (size_t)(row0 + p * G::RPP) * G::D;
+#pragma unroll
+        for (int c = 0; c < G::NCH; ++c) {
+            Words<G::VB> w;
+#pragma unroll
+            for (int i = 0; i < G::VW / 2; ++i) w.w[i] = Sw[p][c * (G::VW / 2) + i];
+            gstore<G::VB, G::NTS>(rowp + c * G::LPR * G::VW + l * G::VW, w);
         }
     }
-    __syncthreads();
+}
 
-    // ---- tokens: S0 k_t and S0 q_t on the stored words, then the per-row recurrence. The
-    // per-head coefficients are formed inline (wave-uniform values): dc[s] = d(t, s) and
-    // dp[s] = d(t-1, s) as running products, gam = gamma_t, gprev = gamma_{t-1}.
-    float dl[P][TCH];  // delta_s of the lane's rows
-    float dc[TCH];
-    float gam = 1.0f;
-    const size_t ostride = (size_t)H * D;
-    uint16_t* obase = o + ((size_t)b * T * H + h) * D;
+// Gram products k_s . k_t and k_s . q_t of the staged tokens, over the workgroup: token pair
+// (s, t) = (pi / TCH, pi % TCH) on the LG lanes of group pi = tid / LG, each lane summing
+// D / LG columns; the pairs reach LDS for every wave (after a barrier).
+template <class G>
+__device__ __forceinline__ void chunk_gram(ChunkLds<G::D, G::TCH>& L, int nt, int tid) {
+    constexpr int D = G::D, TCH = G::TCH;
+    constexpr int LG = G::NT / (TCH * TCH);  // lanes per pair
+    constexpr int CW = D / LG / 2;           // words per lane
+    static_assert(G::NT % (TCH * TCH) == 0 &&
+                  (LG == 1 || LG == 2 || LG == 4 || LG == 8 || LG == 16) && CW % 4 == 0,
+                  "Gram lanes");
+    const int pi = tid / LG, j = tid % LG;
+    const int gs = pi / TCH, gt = pi % TCH;
+    const u32x4* ks = (const u32x4*)&L.kb[gs][2 * CW * j];
+    const u32x4* kt = (const u32x4*)&L.kb[gt][2 * CW * j];
+    const u32x4* qt = (const u32x4*)&L.qb[gt][2 * CW * j];
+    float a = 0.f, c = 0.f;
+    if (gs < nt && gt < nt) {
+#pragma unroll
+        for (int w = 0; w < CW / 4; ++w) {
+            const u32x4 x = ks[w], y = kt[w], z = qt[w];
+            a = dot2_bf16(x.x, y.x, a); a = dot2_bf16(x.y, y.y, a);
+            a = dot2_bf16(x.z, y.z, a); a = dot2_bf16(x.w, y.w, a);
+            c = dot2_bf16(x.x, z.x, c); c = dot2_bf16(x.y, z.y, c);
+            c = dot2_bf16(x.z, z.z, c); c = dot2_bf16(x.w, z.w, c);
+        }
+    }
+    if constexpr (LG >= 2) {
+        a += dpp_mov<0xB1>(a);
+        c += dpp_mov<0xB1>(c);
+    }
+    if constexpr (LG >= 4) {
+        a += dpp_mov<0x4E>(a);
+        c += dpp_mov<0x4E>(c);
+    }
+    if constexpr (LG >= 8) {
+        a += dpp_mov<0x141>(a);
+        c += dpp_mov<0x141>(c);
+    }
+    if constexpr (LG >= 16) {
+        a += dpp_mov<0x140>(a);
+        c += dpp_mov<0x140>(c);
+    }
+    if (j == 0) {
+        L.kk[gs][gt] = a;
+        L.kq[gs][gt] = c;
+    }
+}
+
+// The staged tokens from the stored state words: S0 k_t and S0 q_t on the words, then the
+// per-row recurrence; o_t (and with DELTA the write coefficient delta_t, in fp32) goes to
+// obase (dbase) + t ostride + row on the lane with l == p of each row group. The per-head
+// coefficients are formed inline (wave-uniform values): dc[s] = d(t, s) and dp[s] = d(t-1, s)
+// as running products, gam = gamma_t. On return dl holds delta_s of the lane's rows, dc[s] =
+// d(nt-1, s) and gam = gamma_{nt-1}.
+template <class G, bool DELTA>
+__device__ __forceinline__ void chunk_tokens(const uint32_t (&Sw)[G::P][G::E / 2],
+                                             const ChunkLds<G::D, G::TCH>& L, int nt, int rbase,
+                                             int g, int l, uint16_t* __restrict__ obase,
+                                             float* __restrict__ dbase, size_t ostride,
+                                             float scale, float (&dl)[G::P][G::TCH],
+                                             float (&dc)[G::TCH], float& gam) {
+    constexpr int TCH = G::TCH, P = G::P, W = G::E / 2;
+    gam = 1.0f;
 #pragma unroll
     for (int t = 0; t < TCH; ++t) {
         if (t >= nt) break;
@@ -895,7 +921,7 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
             if (s < t) cu[s] = dp[s] * L.kk[s][t];
             if (s <= t) co[s] = dc[s] * L.kq[s][t];
         }
-        float ov = 0.f;
+        float ov = 0.f, dv = 0.f;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int row = rbase + g + p * G::RPP;
@@ -909,12 +935,48 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
             for (int s = 0; s < TCH; ++s)
                 if (s <= t) op = fmaf(co[s], dl[p][s], op);
             ov = (l == p) ? scale * op : ov;
+            dv = (l == p) ? dl[p][t] : dv;
         }
-        if (l < P) obase[(size_t)t * ostride + rbase + l * G::RPP + g] = act_from_f32<uint16_t>(ov);
+        if (l < P) {
+            const size_t at_o = (size_t)t * ostride + rbase + l * G::RPP + g;
+            obase[at_o] = act_from_f32<uint16_t>(ov);
+            if constexpr (DELTA) dbase[at_o] = dv;
+        }
     }
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
+    int T, int H, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, uint16_t* __restrict__ state, uint16_t* __restrict__ o,
+    float scale) {
+    constexpr int D = G::D, TCH = G::TCH, P = G::P;
+    static_assert(sizeof(typename G::ST) == 2 && G::E % 2 == 0, "bf16 rows");
+    __shared__ ChunkLds<D, TCH> L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / G::LPR, l = lane % G::LPR;
+    const int64_t n = tile_index<G::GRP>(blockIdx.x, gridDim.x);  // b * H + h
+    const int64_t b = n / H;
+    const int h = (int)(n - b * H);
+    uint16_t* Sg = state + (size_t)n * D * D;
+    const int rbase = wave * G::RPW;
+    const int nt = T;  // 2 .. TCH, checked by the launcher
+
+    ChunkStage<G> st;
+    st.fetch(q, k, v, alpha, beta, b, T, H, h, nt, tid);
+    uint32_t Sw[P][G::E / 2];
+    load_state_words<G>(Sg, rbase + g, l, Sw);
+    st.commit(L, nt, tid);
+    __syncthreads();
+    chunk_gram<G>(L, nt, tid);
+    __syncthreads();
+
+    float dl[P][TCH], dc[TCH], gam;
+    chunk_tokens<G, false>(Sw, L, nt, rbase, g, l, o + ((size_t)b * T * H + h) * D, nullptr,
+                           (size_t)H * D, scale, dl, dc, gam);
 
     // ---- S_T = gamma_{T-1} S0 + sum_s d(T-1, s) delta_s k_s^T, rounded once, stored
-    // after the last token dc[s] = d(T-1, s) and gam = gamma_{T-1}
     const float gT = gam;
     float cs[P][TCH];
 #pragma unroll
@@ -931,8 +993,8 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
 #pragma unroll
             for (int i = 0; i < G::VW; i += 2) {
                 const uint32_t wd = Sw[p][c * (G::VW / 2) + i / 2];
-                acc[i] = gT * bf16_to_f32(wd & 0xffffu);
-                acc[i + 1] = gT * __uint_as_float(wd & 0xffff0000u);
+                acc[i] = gT * unpack<uint16_t>(wd, 0);
+                acc[i + 1] = gT * unpack<uint16_t>(wd, 1);
             }
 #pragma unroll
             for (int s = 0; s < TCH; ++s) {
@@ -964,6 +1026,65 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
 }
 
 // ------------------------------------------------------------------------ verify kernel
+
+// The accepted prefix of the previous call for sequence b: n_prev[b] clamped to [0, Tp]
+// (0 when there was no previous call), wave-uniform.
+__device__ __forceinline__ int accepted_prefix(int64_t b, int Tp, const int32_t* __restrict__ n_prev) {
+    if (Tp <= 0) return 0;
+    const int np = __builtin_amdgcn_readfirstlane(n_prev[b]);
+    return np < 0 ? 0 : (np > Tp ? Tp : np);
+}
+
+// Replay the previous call's first np tokens onto the lane's state rows S (fp32 registers):
+//     S <- alpha_t S + dk_t k_t^T      for t < np,
+// from the write coefficients dk that call emitted. The registers hold S / cc with cc the
+// product of the alphas replayed so far, so each replayed token costs one FMA per element
+// (S' <- S' + (dk / cc') k, cc' = cc alpha); cc is folded back when it would leave
+// [2^-64, 2^64] and at the end. The next token's operands are loaded before this token's
+// update (the index is clamped, so the loads are unconditional).
+template <class G, typename AT>
+__device__ __forceinline__ void commit_prefix(float (&S)[G::P][G::E], int np, int64_t b, int H,
+                                              int h, int row0, int l, int Tp,
+                                              const AT* __restrict__ k_prev,
+                                              const float* __restrict__ alpha_prev,
+                                              const float* __restrict__ dk_prev) {
+    constexpr int D = G::D;
+    struct Replay {
+        float kk[G::E], dl[G::P], a;
+    };
+    auto load_replay = [&](int t, Replay& r) {
+        const size_t tok = ((size_t)b * Tp + t) * H + h;
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) r.kk[e] = act_to_f32(k_prev[tok * D + G::col(l, e)]);
+#pragma unroll
+        for (int p = 0; p < G::P; ++p) r.dl[p] = dk_prev[tok * D + row0 + p * G::RPP];
+        r.a = uniform(alpha_prev[tok]);
+    };
+    float cc = 1.0f;
+    Replay cur;
+    load_replay(0, cur);
+    for (int t = 0; t < np; ++t) {
+        Replay nxt;
+        load_replay(min(t + 1, np - 1), nxt);
+        float cn = cc * cur.a;
+        if (!(cn >= 0x1p-64f && cn <= 0x1p64f)) {
+            scale_state<G>(S, cc);
+            scale_state<G>(S, cur.a);
+            cn = 1.0f;
+        }
+        const float inv_cn = __builtin_amdgcn_rcpf(cn);
+#pragma unroll
+        for (int p = 0; p < G::P; ++p) {
+            const float coef = cur.dl[p] * inv_cn;
+#pragma unroll
+            for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(coef, cur.kk[e], S[p][e]);
+        }
+        cc = cn;
+        cur = nxt;
+    }
+    if (cc != 1.0f) scale_state<G>(S, cc);
+}
+
 
 // Speculative verify with a deferred commit. The stored state is the committed state as of the
 // start of the previous call; that call's accepted prefix (n_prev[b] of its Tp tokens, clamped
@@ -1002,53 +1123,23 @@ __global__ __launch_bounds__(G::NT) void gdn_verify_kernel(
     load_state<G>(Sg, row0, l, S);
 
     // Commit the previous call's accepted prefix.
-    int np = 0;
-    if (Tp > 0) {
-        np = __builtin_amdgcn_readfirstlane(n_prev[b]);
-        np = np < 0 ? 0 : (np > Tp ? Tp : np);
-    }
-    // The registers hold S / cc with cc the product of the alphas replayed so far, so each
-    // replayed token costs one FMA per element (S' <- S' + (dk / cc') k, cc' = cc alpha); cc
-    // is folded back when it would leave [2^-64, 2^64] and before the store. The next token's
-    // operands are loaded before this token's update (the index is clamped, so the loads are
-    // unconditional).
-    struct Replay {
-        float kk[G::E], dl[G::P], a;
-    };
-    auto load_replay = [&](int t, Replay& r) {
-        const size_t tok = ((size_t)b * Tp + t) * H + h;
-#pragma unroll
-        for (int e = 0; e < G::E; ++e) r.kk[e] = act_to_f32(k_prev[tok * D + G::col(l, e)]);
-#pragma unroll
-        for (int p = 0; p < G::P; ++p) r.dl[p] = dk_prev[tok * D + row0 + p * G::RPP];
-        r.a = uniform(alpha_prev[tok]);
-    };
-    float cc = 1.0f;
+    const int np = accepted_prefix(b, Tp, n_prev);
+    if (np > 0) commit_prefix<G, AT>(S, np, b, H, h, row0, l, Tp, k_prev, alpha_prev, dk_prev);
     if (np > 0) {
-        Replay cur;
-        load_replay(0, cur);
-        for (int t = 0; t < np; ++t) {
-            Replay nxt;
-            load_replay(min(t + 1, np - 1), nxt);
-            float cn = cc * cur.a;
-            if (!(cn >= 0x1p-64f && cn <= 0x1p64f)) {
-                scale_state<G>(S, cc);
-                scale_state<G>(S, cur.a);
-                cn = 1.0f;
-            }
-            const float inv_cn = __builtin_amdgcn_rcpf(cn);
+        store_state<G>(Sg, row0, l, S);
+        // the new tokens run from the committed state as stored (the state the next call
+        // loads, to which it applies their write coefficients)
+        if constexpr (sizeof(typename G::ST) == 2) {
 #pragma unroll
-            for (int p = 0; p < G::P; ++p) {
-                const float coef = cur.dl[p] * inv_cn;
+            for (int p = 0; p < G::P; ++p)
 #pragma unroll
-                for (int e = 0; e < G::E; ++e) S[p][e] = fmaf(coef, cur.kk[e], S[p][e]);
-            }
-            cc = cn;
-            cur = nxt;
+                for (int e = 0; e < G::E; e += 2) {
+                    const uint32_t w = pack2<typename G::ST>(S[p][e], S[p][e + 1]);
+                    S[p][e] = unpack<typename G::ST>(w, 0);
+                    S[p][e + 1] = unpack<typename G::ST>(w, 1);
+                }
         }
-        if (cc != 1.0f) scale_state<G>(S, cc);
     }
-    if (np > 0) store_state<G>(Sg, row0, l, S);
 
     // Verify the new tokens from the committed state.
     float c = 1.0f;
@@ -1199,6 +1290,63 @@ __global__ __launch_bounds__(G::NT) void gdn_conv_gate_decode_kernel(
     store_state<G>(Sg, rbase + g, l, S);
 }
 
+// The verify kernel for a bf16 state with bf16 activations and 1 .. TCH new tokens, in the
+// chunk form: the committed state as stored is the S0 of the new tokens, whose o and write
+// coefficients come from packed bf16 dots on its words (as in gdn_decode_chunk_kernel); the
+// state after them is never formed (nothing is stored for it).
+template <class G>
+__global__ __launch_bounds__(G::NT) void gdn_verify_chunk_kernel(
+    int T, int H, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+    const float* __restrict__ beta, uint16_t* __restrict__ state, int Tp,
+    const int32_t* __restrict__ n_prev, const uint16_t* __restrict__ k_prev,
+    const float* __restrict__ alpha_prev, const float* __restrict__ dk_prev,
+    uint16_t* __restrict__ o, float* __restrict__ dk_out, float scale) {
+    constexpr int D = G::D, TCH = G::TCH, P = G::P, E = G::E;
+    static_assert(sizeof(typename G::ST) == 2 && E % 2 == 0, "bf16 rows");
+    __shared__ ChunkLds<D, TCH> L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / G::LPR, l = lane % G::LPR;
+    const int64_t n = tile_index<G::GRP>(blockIdx.x, gridDim.x);  // b * H + h
+    const int64_t b = n / H;
+    const int h = (int)(n - b * H);
+    uint16_t* Sg = state + (size_t)n * D * D;
+    const int rbase = wave * G::RPW;
+    const int nt = T;  // 1 .. TCH, checked by the launcher
+
+    ChunkStage<G> st;
+    st.fetch(q, k, v, alpha, beta, b, T, H, h, nt, tid);
+    uint32_t Sw[P][E / 2];
+    load_state_words<G>(Sg, rbase + g, l, Sw);
+
+    const int np = accepted_prefix(b, Tp, n_prev);
+    if (np > 0) {
+        float S[P][E];
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int e = 0; e < E; e += 2) {
+                S[p][e] = unpack<uint16_t>(Sw[p][e / 2], 0);
+                S[p][e + 1] = unpack<uint16_t>(Sw[p][e / 2], 1);
+            }
+        commit_prefix<G, uint16_t>(S, np, b, H, h, rbase + g, l, Tp, k_prev, alpha_prev, dk_prev);
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int e = 0; e < E; e += 2) Sw[p][e / 2] = f32x2_to_bf16x2(S[p][e], S[p][e + 1]);
+        store_state_words<G>(Sg, rbase + g, l, Sw);
+    }
+
+    st.commit(L, nt, tid);
+    __syncthreads();
+    chunk_gram<G>(L, nt, tid);
+    __syncthreads();
+    float dl[P][TCH], dc[TCH], gam;
+    const size_t ob = ((size_t)b * T * H + h) * D;
+    chunk_tokens<G, true>(Sw, L, nt, rbase, g, l, o + ob, dk_out + ob, (size_t)H * D, scale, dl,
+                          dc, gam);
+}
+
 // ------------------------------------------------------------------------ dispatch
 
 template <class G, bool MULTI, typename AT>
@@ -1232,6 +1380,29 @@ hipError_t launch_chunk_g(const DecodeArgs& a, hipStream_t s) {
     void* args[] = {&T, &H, &q, &k, &v, &alpha, &beta, &state, &o, &scale};
     static_assert((int64_t)G::NT <= kThreadsPerHeadPerDim * G::D, "threads per head");
     return hipLaunchKernel((const void*)gdn_decode_chunk_kernel<G>, dim3((unsigned)(a.B * a.H)),
+                           dim3(G::NT), args, 0, s);
+}
+
+template <class G>
+hipError_t launch_verify_chunk_g(const VerifyArgs& a, hipStream_t s) {
+    int T = a.T, H = a.H, Tp = a.Tp;
+    const uint16_t* q = (const uint16_t*)a.q;
+    const uint16_t* k = (const uint16_t*)a.k;
+    const uint16_t* v = (const uint16_t*)a.v;
+    const float* alpha = a.alpha;
+    const float* beta = a.beta;
+    uint16_t* state = (uint16_t*)a.state;
+    const int32_t* n_prev = a.n_prev;
+    const uint16_t* k_prev = (const uint16_t*)a.k_prev;
+    const float* alpha_prev = a.alpha_prev;
+    const float* dk_prev = a.dk_prev;
+    uint16_t* o = (uint16_t*)a.o;
+    float* dk_out = a.dk_out;
+    float scale = a.scale;
+    void* args[] = {&T, &H, &q, &k, &v, &alpha, &beta, &state, &Tp, &n_prev, &k_prev,
+                    &alpha_prev, &dk_prev, &o, &dk_out, &scale};
+    static_assert((int64_t)G::NT <= kThreadsPerHeadPerDim * G::D, "threads per head");
+    return hipLaunchKernel((const void*)gdn_verify_chunk_kernel<G>, dim3((unsigned)(a.B * a.H)),
                            dim3(G::NT), args, 0, s);
 }
 
@@ -1383,6 +1554,10 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
 template <int D, typename ST>
 hipError_t launch_verify_s(const VerifyArgs& a, hipStream_t s) {
     using G = typename VerifyTokens<D, ST>::G;
+    if constexpr (sizeof(ST) == 2 && !is_f16<ST>::value) {
+        if (a.act == DType::BF16 && a.T >= 1 && a.T <= DecodeChunk<D>::G::TCH)
+            return launch_verify_chunk_g<typename DecodeChunk<D>::G>(a, s);
+    }
     switch (a.act) {
         case DType::F32: return launch_verify_g<G, float>(a, s);
         case DType::BF16: return launch_verify_g<G, uint16_t>(a, s);

@@ -13,7 +13,7 @@ import torch
 import gated_deltanet_recurrent_02_amd as gdn
 import oracle
 from gated_deltanet_recurrent_02_amd import synth
-from parity import (check_lowrank, check_o, check_state, f64, gpu_decode, gpu_lowrank,
+from parity import (as_stored, stored_state_slack, check_lowrank, check_o, check_state, f64, gpu_decode, gpu_lowrank,
                     oracle_decode_all, oracle_lowrank, oracle_prefix_all, per_sequence, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -98,9 +98,11 @@ def test_verify_workload_rounds_all_heads(sdt):
     del o1_ref
     S1c = oracle_prefix_all(x1, n1.tolist())
     check_state(S_c1, S1c, DT[sdt], what="committed state after round 1's prefix")
-    x2s = dict(x2, state=torch.from_numpy(S1c))
+    # round 2 runs from the committed state as stored
+    x2s = dict(x2, state=torch.from_numpy(as_stored(S1c, DT[sdt])))
     _, o2_ref = oracle_decode_all(x2s)
-    check_o(o2, o2_ref, torch.bfloat16)
+    check_o(o2, o2_ref, torch.bfloat16,
+            extra=stored_state_slack(x2s["state"].numpy(), f64(x2["q"]), DT[sdt]))
     del o2_ref
     S2c = oracle_prefix_all(x2s, n2.tolist())
     check_state(S_c2, S2c, DT[sdt], what="committed state after round 2's prefix")

@@ -11,7 +11,7 @@ from hypothesis import strategies as st
 import gated_deltanet_recurrent_02_amd as gdn
 import oracle
 from gated_deltanet_recurrent_02_amd import synth
-from parity import (check_lowrank, check_o, check_state, f64, gpu_decode, gpu_lowrank,
+from parity import (as_stored, stored_state_slack, check_lowrank, check_o, check_state, f64, gpu_decode, gpu_lowrank,
                     oracle_decode, oracle_lowrank, oracle_prefix_all, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -120,8 +120,10 @@ def test_verify_random_rounds(B, H, T1, T2, D, sdt, data, seed):
     check_o(f64(o1), o1_ref, torch.bfloat16)
     S1c = oracle_prefix_all(x1, n1)
     check_state(S_c1, S1c, DT[sdt], what="committed state after round 1's prefix")
-    x2s = dict(x2, state=torch.from_numpy(S1c))
+    # round 2 runs from the committed state as stored
+    x2s = dict(x2, state=torch.from_numpy(as_stored(S1c, DT[sdt])))
     _, o2_ref = oracle_decode(x2s)
-    check_o(f64(o2), o2_ref, torch.bfloat16)
+    check_o(f64(o2), o2_ref, torch.bfloat16,
+            extra=stored_state_slack(f64(x2s["state"]), f64(x2["q"]), DT[sdt]))
     check_state(f64(state), oracle_prefix_all(x2s, n2), DT[sdt],
                 what="committed state after round 2's prefix")

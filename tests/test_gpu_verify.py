@@ -12,7 +12,7 @@ import torch
 import gated_deltanet_recurrent_02_amd as gdn
 import oracle
 from gated_deltanet_recurrent_02_amd import synth
-from parity import check_o, check_state, f64, to_dev
+from parity import as_stored, check_o, check_state, f64, stored_state_slack, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -63,20 +63,24 @@ def test_verify_rounds_commit_the_accepted_prefix(D, sdt):
     S0_64 = f64(S0)
     _, o1_ref = oracle.gdn_decode(*[f64(t) for t in _tokens(x1)], S0_64)
     S1c = _oracle_prefix(S0_64, x1, n1.tolist())
-    _, o2_ref = oracle.gdn_decode(*[f64(t) for t in _tokens(x2)], S1c)
-    S2c = _oracle_prefix(S1c, x2, n2.tolist())
+    # the second call's tokens run from the committed state as stored
+    S1s = as_stored(S1c, DT[sdt])
+    _, o2_ref = oracle.gdn_decode(*[f64(t) for t in _tokens(x2)], S1s)
+    S2c = _oracle_prefix(S1s, x2, n2.tolist())
     check_o(f64(o1), o1_ref, torch.bfloat16)
-    check_o(f64(o2), o2_ref, torch.bfloat16)
+    check_o(f64(o2), o2_ref, torch.bfloat16,
+            extra=stored_state_slack(S1s, f64(x2["q"]), DT[sdt]))
     check_state(f64(S_after2), S1c, DT[sdt], what="committed state after the first verify call")
     check_state(f64(state), S2c, DT[sdt], what="committed state after the second verify call")
 
 
-def test_verify_write_coefficients():
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_verify_write_coefficients(sdt):
     # dk_t is the row vector with S_t - alpha_t S_{t-1} = dk_t k_t^T: recover it from the
-    # oracle's step-by-step states and compare.
-    _announce("verify dk_out")
+    # oracle's step-by-step states and compare (bf16 state: the chunk-form kernel).
+    _announce(f"verify dk_out state={sdt}")
     B, H, D, T = 3, 4, 128, 4
-    x = synth.decode_inputs(B, H, D, T, alpha_shift=-1.0, seed=42)
+    x = synth.decode_inputs(B, H, D, T, state_dtype=sdt, alpha_shift=-1.0, seed=42)
     g = to_dev(x)
     state = g["state"].clone()
     _, dk = gdn.decode_verify(*_tokens(g), state)
@@ -95,9 +99,12 @@ def test_verify_write_coefficients():
     assert err <= 1e-4, err
 
 
-def test_full_acceptance_equals_plain_step():
-    _announce("verify + commit all == decode_step")
-    x = to_dev(synth.decode_inputs(8, 48, 128, 4, alpha_shift=-1.0, seed=43))
+@pytest.mark.parametrize("sdt", ["f32", "bf16"])
+def test_full_acceptance_equals_plain_step(sdt):
+    # Both entry points run the same token code on the same stored state, so o agrees bit for
+    # bit; the committed state is the plain step's up to rounding order.
+    _announce(f"verify + commit all == decode_step state={sdt}")
+    x = to_dev(synth.decode_inputs(8, 48, 128, 4, state_dtype=sdt, alpha_shift=-1.0, seed=43))
     S_plain = x["state"].clone()
     o_plain = gdn.decode_step(*_tokens(x), S_plain)
     S_ver = x["state"].clone()
@@ -106,7 +113,7 @@ def test_full_acceptance_equals_plain_step():
     n = torch.full((8,), 4, dtype=torch.int32, device="cuda")
     gdn.decode_verify(*empty, S_ver, prev=(n, x["k"], x["alpha"], dk))
     torch.cuda.synchronize()
-    check_state(f64(S_ver), f64(S_plain), torch.float32)
+    check_state(f64(S_ver), f64(S_plain), DT[sdt])
     assert torch.equal(o_ver.view(torch.int16), o_plain.view(torch.int16))
 
 
