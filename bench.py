@@ -159,7 +159,7 @@ ENTRY_POINTS = {"decode": "gdn_decode_step", "fused": "gdn_conv_gate_decode",
                 "verify": "gdn_decode_verify", "prefill": "gdn_prefill",
                 "lowrank": "gdn_lowrank_decode_step", "probe": "gdn_stream_probe"}
 KERNEL_NAMES = {"decode": ["gdn_decode_"], "fused": ["gdn_conv_gate_decode_kernel"],
-                "verify": ["gdn_verify_kernel"],
+                "verify": ["gdn_verify_"],
                 "prefill": ["gdn_prefill_prep_kernel", "gdn_prefill_state_kernel"],
                 "lowrank": ["gdn_lowrank_"], "probe": ["gdn_stream_probe_kernel"]}
 PROFILE_PREFIX = {"decode": "gdn_decode_kernel", "fused": "gdn_conv_gate_decode_kernel",
@@ -817,9 +817,9 @@ def summarize(root: str, workload: str, state_dtype: str, out_dir: str = PROFILE
                 f"{res['vgpr']} ({res['agpr']}) | {res['sgpr']} | {res['lds']} | {res['wg']} |")
         lines.append("")
     os.makedirs(out_dir, exist_ok=True)
-    # a decode workload runs one of two kernels (token by token, or the chunk form): the file
-    # is named for the one that ran
-    prefix = disp[names[0]] if kind == "decode" else PROFILE_PREFIX[kind]
+    # a decode or verify workload runs one of two kernels (token by token, or the chunk form):
+    # the file is named for the one that ran
+    prefix = disp[names[0]] if kind in ("decode", "verify") else PROFILE_PREFIX[kind]
     path = os.path.join(out_dir, f"{prefix}_{tag}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines).rstrip() + "\n")

@@ -92,7 +92,10 @@ gdn_status gdn_state_free(void* state);
  *   scale  multiplies q in the readout (1.0f = the plain definition)
  *
  * Arithmetic is fp32 (bf16 and fp16 inputs widen exactly); a 16-bit state is widened on load,
- * kept in fp32 across the T tokens of the call and rounded once when stored. An fp16 state or
+ * kept in fp32 across the T tokens of the call and rounded once when stored. With a bf16 state,
+ * bf16 activations and 2 <= T <= 8 the call takes the chunk form of the same recurrence
+ * (products with the loaded state, state updated once; section 三.3 of the same page names the
+ * form): the same result up to the order of rounding. An fp16 state or
  * output saturates to infinity beyond 65504; keeping values in range is the caller's choice
  * of that dtype.
  * Errors: GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP (see conventions).
@@ -114,9 +117,11 @@ gdn_status gdn_decode_step(int64_t B, int32_t T, int32_t H, int32_t dk, int32_t 
  *      are committed by replaying their updates, S <- alpha_t S + dk_t k_t^T for t < n_prev[b],
  *      from the previous call's keys, decays and emitted write coefficients; the result is
  *      stored in `state` (left untouched where the prefix is empty).
- *   2. The T new tokens run from that committed state exactly as in gdn_decode_step, writing o
- *      for every token and their write coefficients dk_out (dk_t = beta_t (v_t - alpha_t S k_t),
- *      so that S_t = alpha_t S_{t-1} + dk_t k_t^T); the state after them is NOT stored.
+ *   2. The T new tokens run from that committed state as stored (rounded to state_dtype: the
+ *      state the next call loads and replays their coefficients onto), as in gdn_decode_step,
+ *      writing o for every token and their write coefficients dk_out
+ *      (dk_t = beta_t (v_t - alpha_t S k_t), so that S_t = alpha_t S_{t-1} + dk_t k_t^T); the
+ *      state after them is NOT stored.
  *
  * A first call passes Tp = 0; a final call that only commits passes T = 0. The caller keeps
  * each call's k, alpha and dk_out for the next call. One state read and at most one state
