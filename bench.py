@@ -88,6 +88,9 @@ EXTRA_CONFIGS = [
     ("fused_b256_t4_f32", "fused_b256_h48_d128_t4", "f32"),
     ("decode_b256_t4_f32", "decode_b256_h48_d128_t4", "f32"),
     ("verify_b256_t4_f32", "verify_b256_h48_d128_t4", "f32"),
+    # bf16 states with bf16 activations take the chunk form for these calls
+    ("decode_b256_t4_bf16_state", "decode_b256_h48_d128_t4", "bf16"),
+    ("verify_b256_t4_bf16_state", "verify_b256_h48_d128_t4", "bf16"),
     ("prefill_b4_t4096_f32", "prefill_b4_h48_d128_t4096", "f32"),
     ("lowrank_b256_r16_t1_f32", "lowrank_b256_h48_d128_r16_t1", "f32"),
     ("lowrank_b256_r16_t4_bf16", "lowrank_b256_h48_d128_r16_t4", "bf16"),
