@@ -133,11 +133,16 @@ def test_replay_folds_out_of_range_decays(sdt):
     g = to_dev(x)
     state = g["state"]
     _, d = gdn.decode_verify(*_tokens(g), state)
-    empty = tuple(t[:, :0].contiguous() for t in _tokens(g))
-    gdn.decode_verify(*empty, state, prev=(n.cuda(), g["k"], g["alpha"], d))
+    # the committing call drafts 3 new tokens (a bf16 state: the chunk-form kernel's replay)
+    x3 = synth.decode_inputs(B, H, D, 3, state_dtype=sdt, alpha_shift=-1.0, seed=46)
+    g3 = to_dev(x3)
+    o3, _ = gdn.decode_verify(*_tokens(g3), state, prev=(n.cuda(), g["k"], g["alpha"], d))
     torch.cuda.synchronize()
     S_ref = _oracle_prefix(f64(x["state"]), x, n.tolist())
     check_state(f64(state), S_ref, DT[sdt], what="committed state")
+    S_st = as_stored(S_ref, DT[sdt])
+    _, o3_ref = oracle.gdn_decode(*[f64(t) for t in _tokens(x3)], S_st)
+    check_o(f64(o3), o3_ref, torch.bfloat16, extra=stored_state_slack(S_st, f64(x3["q"]), DT[sdt]))
 
 
 def test_n_prev_is_clamped():
