@@ -68,11 +68,19 @@ def check_o(o_gpu: np.ndarray, ref: np.ndarray, dtype: torch.dtype, heads_axis_l
             e = float(np.max(d / np.maximum(np.maximum(n, 1e-3 * head), 1e-300)))
         assert e <= TOL_O_F32, f"o: per-token relative error {e:.3e} > {TOL_O_F32}"
         return e
-    e = head_rel_err(o_gpu, ref, 1)
-    tol, ulp = (TOL_O_BF16, 2.0 ** -8) if dtype == torch.bfloat16 else (1e-3, 2.0 ** -11)
+    # ulp: one rounding relative to the value; sub: one rounding in the type's subnormal
+    # range (half its smallest step), where the step is absolute
+    tol, ulp, sub = ((TOL_O_BF16, 2.0 ** -8, 2.0 ** -134) if dtype == torch.bfloat16
+                     else (1e-3, 2.0 ** -11, 2.0 ** -25))
+    diff = np.abs(o_gpu - ref)
+    if np.any(np.isnan(diff)):
+        e = float("inf")
+    else:
+        d = np.maximum(diff - sub, 0.0).max(axis=-1)
+        e = float(np.max(d / np.maximum(np.abs(ref).max(axis=-1), 1e-300)))
     assert e <= tol, f"o: per-head relative error {e:.3e} > {tol}"
     scale = np.abs(ref).max(axis=-1, keepdims=True)
-    bound = ulp * np.abs(ref) + 1e-4 * scale + extra
+    bound = ulp * np.abs(ref) + 1e-4 * scale + sub + extra
     bad = np.abs(o_gpu - ref) > bound
     assert not bad.any(), f"o: {int(bad.sum())} elements beyond one rounding to {dtype}"
     return e

@@ -4,7 +4,7 @@ ties included) and against the formats' definitions at their edges."""
 import numpy as np
 import torch
 
-from parity import as_stored
+from parity import as_stored, check_o
 
 
 def _fp32_values(n=200_000, seed=0):
@@ -36,3 +36,23 @@ def test_as_stored_rounds_fp64_directly():
     # fp16 subnormals are multiples of 2^-24
     y = np.array([2.0 ** -24 * 0.5, 2.0 ** -24 * 0.75, 2.0 ** -24 * 2.5, 2.0 ** -15])
     assert np.array_equal(as_stored(y, torch.float16), [0.0, 2.0 ** -24, 2.0 * 2.0 ** -24, 2.0 ** -15])
+
+
+def test_check_o_accepts_every_correctly_rounded_output():
+    # check_o must admit the exact value rounded once to the output type, subnormals included
+    # (fp16 below 2^-14 rounds to multiples of 2^-24), and reject one unit more.
+    rng = np.random.default_rng(3)
+    # token vectors from 2^-22 (fp16 subnormals) to 2^1 in scale
+    ref = rng.standard_normal((2, 5, 3, 64)) * np.exp2(rng.integers(-22, 2, (2, 5, 3, 1)))
+    for dtype in (torch.bfloat16, torch.float16):
+        check_o(as_stored(ref, dtype), ref, dtype)
+    # 1.5 2^-25 rounds to 2^-24 (error 2^-25): admitted; a whole unit more is not
+    tiny = np.full((1, 1, 1, 4), 1.5 * 2.0 ** -25)
+    check_o(as_stored(tiny, torch.float16), tiny, torch.float16)
+    off = as_stored(tiny, torch.float16) + 2.0 ** -24
+    try:
+        check_o(off, tiny, torch.float16)
+    except AssertionError:
+        pass
+    else:
+        raise AssertionError("one unit beyond the rounding passed")
