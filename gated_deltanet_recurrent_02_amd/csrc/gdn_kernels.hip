@@ -31,6 +31,9 @@
 // The fused kernel replaces the staging by the conv (kernel 4) + SiLU + L2-norm + gate
 // prologue of the same chain, computed by the workgroup for the 3*D channels its head owns; it
 // is also the only reader and writer of those channels' conv state.
+// A few tokens (up to 8) on a bf16 state with bf16 activations take the chunk form instead
+// (gdn_decode_chunk_kernel, gdn_verify_chunk_kernel): products with the stored state as packed
+// bf16 dots on the loaded words, and the state updated once; see there.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
