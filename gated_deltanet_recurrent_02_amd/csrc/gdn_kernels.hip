@@ -676,9 +676,10 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_kernel(
 
 // ------------------------------------------------------------------------ chunk-form decode
 
-// A few tokens (2 .. TCH) on a bf16 state with bf16 activations. The token-by-token form needs
-// S_{t-1} k_t and S_t q_t, two FMAs per state element and token on the current fp32 state. Over
-// one call they unroll to products with the stored state S0 (the chunk form of the same
+// A few tokens (3 .. TCH for decode, 1 .. TCH for verify) on a bf16 state with bf16
+// activations. The token-by-token form needs S_{t-1} k_t and S_t q_t, two FMAs per state
+// element and token on the current fp32 state. Over one call they unroll to products with the
+// stored state S0 (the chunk form of the same
 // recurrence; "GDN tuning limits on Kunlun XPU", section 三.3 names it):
 //     gamma_t = alpha_0 ... alpha_t,  d(t, s) = alpha_{s+1} ... alpha_t  (d(t, t) = 1),
 //     S_{t-1} k_t = gamma_{t-1} S0 k_t + sum_{s<t} d(t-1, s) (k_s . k_t) delta_s,
@@ -964,7 +965,7 @@ __global__ __launch_bounds__(G::NT) void gdn_decode_chunk_kernel(
     const int h = (int)(n - b * H);
     uint16_t* Sg = state + (size_t)n * D * D;
     const int rbase = wave * G::RPW;
-    const int nt = T;  // 2 .. TCH, checked by the launcher
+    const int nt = T;  // 3 .. TCH, checked by the launcher
 
     ChunkStage<G> st;
     st.fetch(q, k, v, alpha, beta, b, T, H, h, nt, tid);
@@ -1504,7 +1505,7 @@ template <int D> struct DecodeTokens<D, float> {
     using G = Geo<D, float, 1, max_int(1, D / 16), 8, true, true, 2, 16>;
 };
 
-// Chunk form (bf16 state and activations, 2 .. TCH tokens): the multi-token geometry.
+// Chunk form (bf16 state and activations, up to TCH tokens): the multi-token geometry.
 template <int D> struct DecodeChunk {
     using G = Geo<D, uint16_t, max_int(1, D / 16), 1, 8, true, true, 4, 8>;
 };

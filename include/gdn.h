@@ -93,7 +93,7 @@ gdn_status gdn_state_free(void* state);
  *
  * Arithmetic is fp32 (bf16 and fp16 inputs widen exactly); a 16-bit state is widened on load,
  * kept in fp32 across the T tokens of the call and rounded once when stored. With a bf16 state,
- * bf16 activations and 2 <= T <= 8 the call takes the chunk form of the same recurrence
+ * bf16 activations and 3 <= T <= 8 the call takes the chunk form of the same recurrence
  * (products with the loaded state, state updated once; section 三.3 of the same page names the
  * form): the same result up to the order of rounding. An fp16 state or
  * output saturates to infinity beyond 65504; keeping values in range is the caller's choice
