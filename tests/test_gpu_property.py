@@ -17,7 +17,7 @@ from parity import (as_stored, stored_state_slack, check_lowrank, check_o, check
 pytestmark = pytest.mark.gpu
 
 DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
-SETTINGS = settings(max_examples=40, deadline=None, derandomize=True, database=None,
+SETTINGS = settings(max_examples=150, deadline=None, derandomize=True, database=None,
                     suppress_health_check=[HealthCheck.too_slow])
 
 
